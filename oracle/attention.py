@@ -1,0 +1,236 @@
+"""Float64 numpy oracle for scaled-dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE: only tests, the smoke check and the benchmark's CPU
+baseline use this module.  It shares no code with the HIP library.
+
+What is computed (page tags are defined in ``oracle/__init__.py``):
+
+  Attention(Q, K, V) = softmax(s * Q K^T) V,  s = 1/sqrt(d)
+      [P3] "概念揭曉", the scaled dot-product attention formula;
+      [P2] section 五, the three-line standard attention (S, P, O).
+
+The pages call the tiled method exact ([P1] "为什么这个故事对应
+FlashAttention" list; [P3] "精確注意力" row of the metaphor table), so the
+oracle is the plain definition written out: it materialises S and P for one
+(batch, head) at a time, in float64, on inputs upcast exactly from bf16/fp32.
+
+Conventions chosen where the pages are silent:
+  * ``scale`` is the same fp32 value the GPU path receives, used as a float64.
+  * The saved per-row statistic is the natural-log logsumexp,
+    LSE_i = m_i + ln(l_i) = ln sum_j exp(S_ij)  ([P1] technical notes say only
+    that O and "statistics" go back to HBM; [P2] section 六 keeps m and l).
+  * The backward is the analytic gradient of the formula above (the pages only
+    say that P is recomputed, [P2] section 七):
+        D  = rowsum(dO * O)
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D 1^T)
+        dQ = s dS K,   dK = s dS^T Q
+  * Arrays are [..., N, d]; leading axes are looped over one head at a time.
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "softmax_rows",
+    "sdpa_forward_head",
+    "sdpa_forward",
+    "sdpa_rows",
+    "sdpa_backward_head",
+    "sdpa_backward",
+    "online_forward_head",
+    "online_forward_normalised_head",
+    "two_pass_forward_head",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Row softmax of S with the max subtracted ([P2] section 六, the
+    classic softmax formula; [P3] "兩大核心魔法": subtract the maximum to
+    avoid overflow).  Returns (P, m, l): P = exp(S - m) / l, m the row max,
+    l the row sum of exp(S - m)."""
+    m = S.max(axis=-1)
+    E = np.exp(S - m[..., None])
+    l = E.sum(axis=-1)
+    return E / l[..., None], m, l
+
+
+def sdpa_forward_head(q, k, v, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One head, plain definition.  q [Nq,d], k [Nk,d], v [Nk,dv].
+
+    Steps: S = s Q K^T ([P2] section 五, first line); P = softmax(S) (second
+    line); O = P V (third line); LSE = m + ln l.  Returns (O [Nq,dv], LSE [Nq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = float(scale) * (q @ k.T)
+    P, m, l = softmax_rows(S)
+    O = P @ v
+    lse = m + np.log(l)
+    return O, lse
+
+
+def _heads(x: np.ndarray) -> Tuple[Tuple[int, ...], np.ndarray]:
+    lead = x.shape[:-2]
+    return lead, x.reshape((-1,) + x.shape[-2:])
+
+
+def sdpa_forward(q, k, v, scale: float, heads: Optional[Iterable[int]] = None):
+    """Plain forward over [..., N, d] arrays, one (batch, head) at a time.
+
+    ``heads`` optionally restricts the work to some flattened (b*H + h)
+    indices; the other outputs are left as NaN.  Returns (O, LSE).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead, qf = _heads(q)
+    _, kf = _heads(k)
+    _, vf = _heads(v)
+    O = np.full(qf.shape[:-1] + (vf.shape[-1],), np.nan)
+    L = np.full(qf.shape[:-1], np.nan)
+    for i in (range(qf.shape[0]) if heads is None else heads):
+        O[i], L[i] = sdpa_forward_head(qf[i], kf[i], vf[i], scale)
+    return O.reshape(lead + O.shape[-2:]), L.reshape(lead + L.shape[-1:])
+
+
+def sdpa_rows(q_rows, k, v, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward for selected query rows of one head against the full K and V.
+
+    Each output row depends only on its own query row and all keys, so a row
+    subset is the plain definition restricted to those rows."""
+    return sdpa_forward_head(q_rows, k, v, scale)
+
+
+def sdpa_backward_head(q, k, v, dO, scale: float):
+    """One head, analytic gradient of O = softmax(s Q K^T) V.
+
+    Recomputes S and P from Q and K as the forward does ([P2] section 七:
+    P is recomputed rather than stored), then applies the chain rule.
+    Returns dict with dQ, dK, dV, and the intermediates O, LSE, D, P, dP, dS.
+    """
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    s = float(scale)
+    S = s * (q @ k.T)
+    P, m, l = softmax_rows(S)
+    O = P @ v
+    lse = m + np.log(l)
+    D = (dO * O).sum(axis=-1)              # rowsum(dO * O)
+    dV = P.T @ dO                          # through O = P V, w.r.t. V
+    dP = dO @ v.T                          # through O = P V, w.r.t. P
+    dS = P * (dP - D[:, None])             # softmax Jacobian applied row-wise
+    dQ = s * (dS @ k)                      # through S = s Q K^T, w.r.t. Q
+    dK = s * (dS.T @ q)                    # through S = s Q K^T, w.r.t. K
+    return dict(dQ=dQ, dK=dK, dV=dV, O=O, LSE=lse, D=D, P=P, dP=dP, dS=dS)
+
+
+def sdpa_backward(q, k, v, dO, scale: float, heads: Optional[Iterable[int]] = None):
+    """Analytic backward over [..., N, d] arrays.  Returns (dQ, dK, dV, D).
+
+    Heads not in ``heads`` are left as NaN."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    lead, qf = _heads(q)
+    _, kf = _heads(k)
+    _, vf = _heads(v)
+    _, gf = _heads(dO)
+    dQ = np.full(qf.shape, np.nan)
+    dK = np.full(kf.shape, np.nan)
+    dV = np.full(vf.shape, np.nan)
+    D = np.full(qf.shape[:-1], np.nan)
+    for i in (range(qf.shape[0]) if heads is None else heads):
+        r = sdpa_backward_head(qf[i], kf[i], vf[i], gf[i], scale)
+        dQ[i], dK[i], dV[i], D[i] = r["dQ"], r["dK"], r["dV"], r["D"]
+    return (dQ.reshape(q.shape), dK.reshape(k.shape), dV.reshape(v.shape),
+            D.reshape(lead + D.shape[-1:]))
+
+
+# ---------------------------------------------------------------------------
+# Online-softmax forms, used to check the tiled recurrence against the plain
+# definition.  They walk the key/value rows in blocks ([P2] section 六,
+# "Tiling": K and V cut into T_c blocks), carrying the running max m, the
+# running sum l and the output ([P2] section 六, update rule; [P1] fable
+# section 三: only two running numbers are kept between stacks).
+# ---------------------------------------------------------------------------
+
+def _blocks(n: int, block: int, order: Optional[Sequence[int]]):
+    spans = [(a, min(a + block, n)) for a in range(0, n, block)]
+    if order is not None:
+        spans = [spans[i] for i in order]
+    return spans
+
+
+def online_forward_head(q, k, v, scale: float, block: int = 8,
+                        order: Optional[Sequence[int]] = None):
+    """One pass with an unnormalised output accumulator.
+
+    For each key block b: S_b = s Q K_b^T; m' = max(m, rowmax S_b);
+    alpha = exp(m - m'); P~ = exp(S_b - m'); l = alpha l + rowsum P~;
+    U = alpha U + P~ V_b; m = m'.  The rescale by exp(m_old - m_new) of the
+    output accumulated so far is the identity of [P3] "兩大核心魔法"
+    (e^{x-m_new} = e^{x-m_old} e^{m_old-m_new}).  At the end O = U / l and
+    LSE = m + ln l.  Initial state m = -inf, l = 0, U = 0 (exp(-inf) = 0).
+    ``order`` permutes the blocks ([P1] fable section 四: the merge does not
+    depend on the order the stacks arrive in)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq = q.shape[0]
+    m = np.full(nq, -np.inf)
+    l = np.zeros(nq)
+    U = np.zeros((nq, v.shape[1]))
+    for a, b in _blocks(k.shape[0], block, order):
+        Sb = float(scale) * (q @ k[a:b].T)
+        m_new = np.maximum(m, Sb.max(axis=1))
+        alpha = np.exp(m - m_new)
+        Pt = np.exp(Sb - m_new[:, None])
+        l = alpha * l + Pt.sum(axis=1)
+        U = alpha[:, None] * U + Pt @ v[a:b]
+        m = m_new
+    return U / l[:, None], m + np.log(l)
+
+
+def online_forward_normalised_head(q, k, v, scale: float, block: int = 8,
+                                   order: Optional[Sequence[int]] = None):
+    """One pass keeping O normalised after every block ([P2] section 六,
+    the O_new formula): O_new = diag(alpha) O_old * (l_old / l_new)
+    + P~ V_b / l_new, with l_new = alpha l_old + rowsum P~.  The page writes
+    the first term as O_old / (l_new / l_old); it is evaluated here as
+    O_old * (l_old / l_new), which is the same number and avoids 0/0 on the
+    first block where l_old = 0."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq = q.shape[0]
+    m = np.full(nq, -np.inf)
+    l = np.zeros(nq)
+    O = np.zeros((nq, v.shape[1]))
+    for a, b in _blocks(k.shape[0], block, order):
+        Sb = float(scale) * (q @ k[a:b].T)
+        m_new = np.maximum(m, Sb.max(axis=1))
+        alpha = np.exp(m - m_new)
+        Pt = np.exp(Sb - m_new[:, None])
+        l_new = alpha * l + Pt.sum(axis=1)
+        O = (alpha * l / l_new)[:, None] * O + (Pt @ v[a:b]) / l_new[:, None]
+        l, m = l_new, m_new
+    return O, m + np.log(l)
+
+
+def two_pass_forward_head(q, k, v, scale: float, block: int = 8,
+                          order: Optional[Sequence[int]] = None):
+    """Two passes over the key blocks: the first keeps only the running max
+    and running sum (the "two numbers" of [P1] fable section 三), the second
+    forms P_b = exp(S_b - m) / l per block and accumulates O += P_b V_b."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq = q.shape[0]
+    m = np.full(nq, -np.inf)
+    l = np.zeros(nq)
+    spans = _blocks(k.shape[0], block, order)
+    for a, b in spans:
+        Sb = float(scale) * (q @ k[a:b].T)
+        m_new = np.maximum(m, Sb.max(axis=1))
+        l = np.exp(m - m_new) * l + np.exp(Sb - m_new[:, None]).sum(axis=1)
+        m = m_new
+    O = np.zeros((nq, v.shape[1]))
+    for a, b in spans:
+        Sb = float(scale) * (q @ k[a:b].T)
+        O += (np.exp(Sb - m[:, None]) / l[:, None]) @ v[a:b]
+    return O, m + np.log(l)
