@@ -1,0 +1,207 @@
+"""Throughput of exact attention forward and forward+backward on one MI355X.
+
+A step is one pass of the whole path on one batch: fa_fwd (tiling + online
+softmax) followed by fa_bwd (preprocess, dK/dV with recomputation, dQ).  The
+workload is B=1, H=16, N=8192, d=128, bf16, seeded N(0,1) inputs already
+resident in device memory.  Counted work: 4*B*H*N^2*d FLOP forward and 2.5x
+that backward.
+
+Prints one JSON line with the metric, the roofline of the dominant kernel
+(its algorithmic FLOPs per launch over its average launch time, timed with
+HIP events on the stream it runs on) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+METRIC = "attention TFLOP/s fwd & fwd+bwd, % of bf16 MFMA peak, N=8192 d=128"
+WORKLOAD = "attn_bf16_b1h16_n8192_d128_fwdbwd"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the workload the CPU oracle runs (forward+backward)")
+    return ap.parse_args()
+
+
+def time_launches(fn, n, stream):
+    """Average duration (ms) of n launches of fn, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def cpu_baseline(w, heads):
+    """The fp64 oracle (forward + backward, materialising S and P) on `heads`
+    of the workload's heads; returns a dict in the metric's unit."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q, k, v, dO = synth.make_inputs(w)
+    sel = list(range(heads))
+    f64 = synth.to_f64
+    qf, kf, vf, gf = (f64(x)[:, :heads] for x in (q, k, v, dO))
+    t0 = time.perf_counter()
+    oracle.sdpa_forward(qf, kf, vf, w.scale)
+    oracle.sdpa_backward(qf, kf, vf, gf, w.scale)
+    dt = time.perf_counter() - t0
+    flops = (w.fwd_flops() + w.bwd_flops()) * heads / (w.B * w.H)
+    del np, sel
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of B={w.B},H={w.H},N={w.N},d={w.d}, "
+                      f"forward+backward, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path is built and measured on a "
+              "single MI355X (heads shard across GPUs with no communication, which is not "
+              "built here). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+
+    w = synth.WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, dO = (x.to(dev) for x in synth.make_inputs(w))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    s = w.scale
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    delta = ws.view(torch.float32)[: B * H * N].view(B, H, N)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    mem_base = torch.cuda.memory_allocated()
+
+    def fwd():
+        fa.fa_fwd(q, k, v, s, o=o, lse=lse)
+
+    def bwd():
+        fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, synchronised on both sides.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    # Per-kernel launch times (each entry point launches one kernel except
+    # fa_bwd, whose three stages are timed through their own entry points).
+    n = max(args.steps, 5)
+    ms_fwd = time_launches(fwd, n, stream)
+    ms_pre = time_launches(lambda: fa.fa_bwd_preprocess(o, dO, delta), n, stream)
+    ms_dkdv = time_launches(lambda: fa.fa_bwd_dkdv(q, k, v, lse, dO, delta, s, dk=dk, dv=dv),
+                            n, stream)
+    ms_dq = time_launches(lambda: fa.fa_bwd_dq(q, k, v, lse, dO, delta, s, dq=dq), n, stream)
+    ms_bwd = time_launches(bwd, n, stream)
+
+    pairs = B * H * N * N
+    f_fwd = w.fwd_flops()
+    f_bwd = w.bwd_flops()
+    # algorithmic FLOPs per launch: forward 4d per (query, key) pair; the
+    # dK/dV kernel does four of the backward's five counted contractions
+    # (S, dP, dV, dK: 8d per pair); the dQ kernel does the fifth (2d per pair)
+    # and recomputes S and dP, which are not counted again.
+    kernels = {
+        "fwd_bf16": {"ms": ms_fwd, "flop": 4.0 * d * pairs},
+        "bwd_dkdv_bf16": {"ms": ms_dkdv, "flop": 8.0 * d * pairs},
+        "bwd_dq_bf16": {"ms": ms_dq, "flop": 2.0 * d * pairs},
+        "bwd_pre_bf16": {"ms": ms_pre, "flop": 0.0},
+    }
+    for kk in kernels.values():
+        kk["tflops"] = kk["flop"] / (kk["ms"] * 1e-3) / 1e12
+    dom = max(("fwd_bf16", "bwd_dkdv_bf16", "bwd_dq_bf16"), key=lambda x: kernels[x]["ms"])
+    ach = kernels[dom]["tflops"]
+
+    tf_step = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    tf_fwd = f_fwd / (ms_fwd * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tf_step, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) Q, K, V, dO rounded to bf16",
+        "config": {"workload": WORKLOAD, "B": B, "H": H, "N": N, "d": d, "causal": False,
+                   "scale": s, "counted_flop_fwd": f_fwd, "counted_flop_fwdbwd": f_fwd + f_bwd},
+        "fwdbwd_tflops": round(tf_step, 2),
+        "fwdbwd_frac_of_peak": round(tf_step / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(tf_fwd, 2),
+        "fwd_frac_of_peak": round(tf_fwd / PEAK_BF16_TFLOPS, 4),
+        "ms_fwd": round(ms_fwd, 4),
+        "ms_bwd": round(ms_bwd, 4),
+        "wall_s_timed_region": round(wall, 4),
+        "kernels": {kname: {"ms": round(kv["ms"], 4), "tflops": round(kv["tflops"], 2)}
+                    for kname, kv in kernels.items()},
+        "peak_mem_bytes": int(peak_mem),
+        "mem_inputs_outputs_bytes": int(mem_base),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * fa.h - C ABI of an exact, IO-aware scaled-dot-product attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch b and head h, with S = scale * Q K^T:
+ *     O   = softmax(S) V                          (forward)
+ *     LSE = ln sum_j exp(S_ij)   (one fp32 per query row, natural log)
+ *     dQ, dK, dV = gradients of sum(O * dO)      (backward)
+ * The formula is the scaled dot-product attention of the star-observatory
+ * FlashAttention fable page (ckw19810413.github.io, section 概念揭曉).  The
+ * forward tiles Q, K and V and keeps the running max, running sum and output
+ * on chip, rescaling by exp(m_old - m_new) (same page, section "兩大核心魔法";
+ * 账房先生的奔命 (carrie-l.github.io), section 六), so no N x N matrix is
+ * ever written to device memory.  The backward recomputes P from Q, K and
+ * the saved LSE instead of storing it (账房先生的奔命, section 七).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer.  Q, K, V, O, dO, dQ, dK, dV are
+ *     contiguous [B][H][N][d] (d fastest); LSE is [B][H][N] float32.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates device memory and keeps no state between calls; calls
+ *     are reentrant.
+ *   - Outputs are fully overwritten (never accumulated into) and must not
+ *     overlap any input or each other (FA_ERR_ALIAS).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; nothing synchronises with the host.
+ *   - Arguments are checked before anything is enqueued.  A return other than
+ *     FA_OK means nothing was enqueued.  Faults during execution surface at
+ *     the caller's next synchronisation.  A launch failure is FA_ERR_HIP.
+ *   - B, H or N equal to 0 is an empty problem: FA_OK, nothing enqueued, and
+ *     pointers may be NULL.  Negative sizes are FA_ERR_SHAPE.
+ *   - `scale` must be finite and > 0 (FA_ERR_SCALE); 1/sqrt(d) rounded to
+ *     float is the usual value.
+ *   - No C++ exception crosses this boundary and the library prints nothing.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  FA_ERR_SHAPE = 2,       /* a size is negative, or offsets overflow          */
+  FA_ERR_UNSUPPORTED = 3, /* head dim not supported by this entry point        */
+  FA_ERR_ALIGN = 4,       /* a pointer is not aligned as required              */
+  FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  FA_ERR_SCALE = 6,       /* scale not finite or not > 0                       */
+  FA_ERR_ALIAS = 7,       /* an output overlaps an input or another output     */
+  FA_ERR_HIP = 8          /* the HIP runtime rejected a launch                 */
+} fa_status;
+
+/* A hipStream_t, passed as an opaque pointer so this header needs no HIP. */
+typedef void* fa_stream_t;
+
+/* Human-readable text for a status; never NULL, static storage. */
+const char* fa_status_str(fa_status s);
+
+/* ------------------------------------------------------------------------ */
+/* bf16 path: Q, K, V, O, dO, dQ, dK, dV hold bfloat16 (uint16 storage).    */
+/* Head dim d must be 64 or 128.  Tensor pointers 16-byte aligned; LSE and   */
+/* the workspace 16-byte aligned.  Accumulation is fp32 throughout; P and dS */
+/* are rounded to bf16 (round to nearest even) before their contractions.    */
+/* ------------------------------------------------------------------------ */
+
+/* Forward.  Inputs q, k, v; outputs o (bf16) and lse (fp32, natural log).
+ * Tiling and online softmax: 账房先生的奔命, section 六; rescale identity:
+ * star-observatory fable page, section "兩大核心魔法"; only O and the row
+ * statistic return to memory: 算珠楼的掌簿人 (hespethorn.github.io), 技术解读. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 fa_stream_t stream);
+
+/* Bytes of workspace fa_bwd needs: one fp32 per query row (D = rowsum(dO*O)),
+ * rounded up to 256.  0 for an empty problem.  (size_t)-1 for invalid sizes. */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/* Backward with recomputation (账房先生的奔命, section 七: P is recomputed from
+ * Q, K and the saved LSE, never stored).  Inputs q, k, v, the forward's o and
+ * lse, and dO; outputs dq, dk, dv (bf16).  Runs fa_bwd_preprocess,
+ * fa_bwd_dkdv and fa_bwd_dq in that order on `stream`; deterministic (no
+ * atomics).  `workspace` must hold fa_bwd_workspace_bytes(B,H,N,d) bytes.   */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 fa_stream_t stream);
+
+/* The three stages of fa_bwd, exposed so that each launch can be timed and
+ * tested on its own.  `delta` is [B][H][N] fp32 (16-byte aligned).
+ * fa_bwd_preprocess: delta_i = sum_c dO_ic * O_ic (the O the forward stored). */
+fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                            int64_t B, int64_t H, int64_t N, int64_t d,
+                            fa_stream_t stream);
+/* fa_bwd_dkdv: per key tile, recompute P^T from K, Q and lse, then
+ * dV = P^T dO and dK = scale * dS^T Q with dS = P * (dO V^T - delta).        */
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dO, const float* delta, void* dk, void* dv,
+                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                      fa_stream_t stream);
+/* fa_bwd_dq: per query tile, recompute P and dS and form dQ = scale * dS K.  */
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dO, const float* delta, void* dq,
+                    int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                    fa_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* fp32 path: every tensor is float32, 1 <= d <= 128, pointers 4-byte        */
+/* aligned.  Plain FMA arithmetic with natural exp, key blocks of 8 (the     */
+/* 8 stacks of 8 of 算珠楼的掌簿人, fable section 二).  Meant for tight checks  */
+/* of the method at small sizes rather than for speed.                       */
+/* ------------------------------------------------------------------------ */
+
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     fa_stream_t stream);
+
+/* Same sizing rule as fa_bwd_workspace_bytes. */
+size_t fa_bwd_f32_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                     const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     fa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

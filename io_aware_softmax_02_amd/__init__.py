@@ -1,0 +1,211 @@
+"""Exact IO-aware attention for MI355X (gfx950): Python binding.
+
+The functions here carry the names of the C ABI (include/fa.h) and only
+marshal arguments: they check tensor dtype/device/shape, allocate outputs with
+torch (device memory is plumbing), take the current HIP stream, and call the
+library.  Every step of the computation runs in the library's HIP kernels;
+there is no other implementation, and importing this package fails if the
+library has not been built.
+
+Tensors are contiguous [B, H, N, d] on a GPU; ``lse`` is [B, H, N] float32.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import LIB, FAError, FA_OK, status_str  # noqa: F401
+
+__all__ = [
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
+    "fa_bwd_dq", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
+    "default_scale", "FAError", "status_str",
+]
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded once to fp32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _shape4(x: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {x.device})")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {x.dtype})")
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d] (got {tuple(x.shape)})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return tuple(x.shape)
+
+
+def _same(shape, x: torch.Tensor, name: str, dtype: torch.dtype):
+    if _shape4(x, name, dtype) != shape:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
+
+
+def _rows(x: torch.Tensor, name: str, shape) -> None:
+    B, H, N, _ = shape
+    if x.device.type != "cuda" or x.dtype != torch.float32 or tuple(x.shape) != (B, H, N) \
+            or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 [B, H, N] GPU tensor")
+
+
+def _stream(dev: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(x: Optional[torch.Tensor]) -> int:
+    return 0 if x is None else int(x.data_ptr())
+
+
+def _fwd(fn, where, dtype, q, k, v, scale, o, lse, stream):
+    shape = _shape4(q, "q", dtype)
+    _same(shape, k, "k", dtype)
+    _same(shape, v, "v", dtype)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _same(shape, o, "o", dtype)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _rows(lse, "lse", shape)
+    with torch.cuda.device(q.device):
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                  _stream(q.device, stream)), where)
+    return o, lse
+
+
+def fa_fwd(q, k, v, scale: Optional[float] = None, o=None, lse=None, stream=None
+           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 forward.  Returns (o, lse); o bf16 [B,H,N,d], lse fp32 [B,H,N]."""
+    return _fwd(LIB.fa_fwd, "fa_fwd", torch.bfloat16, q, k, v, scale, o, lse, stream)
+
+
+def fa_fwd_f32(q, k, v, scale: Optional[float] = None, o=None, lse=None, stream=None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp32 forward (key blocks of 8).  Returns (o, lse)."""
+    return _fwd(LIB.fa_fwd_f32, "fa_fwd_f32", torch.float32, q, k, v, scale, o, lse, stream)
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(LIB.fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(LIB.fa_bwd_f32_workspace_bytes(B, H, N, d))
+
+
+def _bwd(fn, wsfn, where, dtype, q, k, v, o, lse, dO, scale, dq, dk, dv, workspace, stream):
+    shape = _shape4(q, "q", dtype)
+    for x, name in ((k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
+        _same(shape, x, name, dtype)
+    _rows(lse, "lse", shape)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    outs = []
+    for x, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if x is None:
+            x = torch.empty_like(q)
+        else:
+            _same(shape, x, name, dtype)
+        outs.append(x)
+    dq, dk, dv = outs
+    need = int(wsfn(B, H, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
+                  _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, float(scale),
+                  _stream(q.device, stream)), where)
+    return dq, dk, dv
+
+
+def fa_bwd(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """bf16 backward with recomputation.  Returns (dq, dk, dv)."""
+    return _bwd(LIB.fa_bwd, LIB.fa_bwd_workspace_bytes, "fa_bwd", torch.bfloat16, q, k, v, o,
+                lse, dO, scale, dq, dk, dv, workspace, stream)
+
+
+def fa_bwd_f32(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=None, dv=None,
+               workspace=None, stream=None):
+    """fp32 backward.  Returns (dq, dk, dv)."""
+    return _bwd(LIB.fa_bwd_f32, LIB.fa_bwd_f32_workspace_bytes, "fa_bwd_f32", torch.float32,
+                q, k, v, o, lse, dO, scale, dq, dk, dv, workspace, stream)
+
+
+def fa_bwd_preprocess(o, dO, delta=None, stream=None):
+    """Stage 1 of fa_bwd: delta = rowsum(dO * o), fp32 [B,H,N]."""
+    shape = _shape4(o, "o", torch.bfloat16)
+    _same(shape, dO, "dO", torch.bfloat16)
+    B, H, N, d = shape
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    else:
+        _rows(delta, "delta", shape)
+    with torch.cuda.device(o.device):
+        _check(LIB.fa_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(delta), B, H, N, d,
+                                     _stream(o.device, stream)), "fa_bwd_preprocess")
+    return delta
+
+
+def fa_bwd_dkdv(q, k, v, lse, dO, delta, scale: Optional[float] = None, dk=None, dv=None,
+                stream=None):
+    """Stage 2 of fa_bwd.  Returns (dk, dv)."""
+    shape = _shape4(q, "q", torch.bfloat16)
+    for x, name in ((k, "k"), (v, "v"), (dO, "dO")):
+        _same(shape, x, name, torch.bfloat16)
+    _rows(lse, "lse", shape)
+    _rows(delta, "delta", shape)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _same(shape, dk, "dk", torch.bfloat16)
+    _same(shape, dv, "dv", torch.bfloat16)
+    with torch.cuda.device(q.device):
+        _check(LIB.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(delta),
+                               _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                               _stream(q.device, stream)), "fa_bwd_dkdv")
+    return dk, dv
+
+
+def fa_bwd_dq(q, k, v, lse, dO, delta, scale: Optional[float] = None, dq=None, stream=None):
+    """Stage 3 of fa_bwd.  Returns dq."""
+    shape = _shape4(q, "q", torch.bfloat16)
+    for x, name in ((k, "k"), (v, "v"), (dO, "dO")):
+        _same(shape, x, name, torch.bfloat16)
+    _rows(lse, "lse", shape)
+    _rows(delta, "delta", shape)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    _same(shape, dq, "dq", torch.bfloat16)
+    with torch.cuda.device(q.device):
+        _check(LIB.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(delta),
+                             _ptr(dq), B, H, N, d, float(scale), _stream(q.device, stream)),
+               "fa_bwd_dq")
+    return dq

@@ -1,0 +1,186 @@
+// C ABI entry points declared in include/fa.h: argument checks (validate.h),
+// then launches on the caller's stream.  Nothing is allocated here.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "validate.h"
+
+namespace fa {
+int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
+int launch_bwd_pre_bf16(const void* o, const void* dO, float* delta, int64_t rows, int64_t d,
+                        hipStream_t stream);
+int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const float* lse,
+                         const void* dO, const float* delta, void* dk, void* dv, int64_t BH,
+                         int64_t N, int64_t d, float scale, hipStream_t stream);
+int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const float* lse,
+                       const void* dO, const float* delta, void* dq, int64_t BH, int64_t N,
+                       int64_t d, float scale, hipStream_t stream);
+int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
+int launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                   const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                   float* delta, int64_t BH, int64_t N, int64_t d, float scale,
+                   hipStream_t stream);
+}  // namespace fa
+
+namespace {
+
+using fa::Shape;
+using fa::Span;
+
+inline fa_status from_hip(int e) { return e == 0 ? FA_OK : FA_ERR_HIP; }
+inline hipStream_t as_stream(fa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+struct Sizes {
+  size_t tensor, rows;
+};
+inline Sizes sizes(const Shape& s, size_t elem) {
+  return {static_cast<size_t>(s.elems()) * elem, static_cast<size_t>(s.rows()) * sizeof(float)};
+}
+
+fa_status check_fwd(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const Shape& s, float scale, bool bf16) {
+  FA_TRY(fa::check_shape(s, bf16));
+  FA_TRY(fa::check_scale(scale));
+  if (s.empty()) return FA_OK;
+  const size_t al = bf16 ? 16 : 4;
+  FA_TRY(fa::check_ptrs({q, k, v, o}, al));
+  FA_TRY(fa::check_ptrs({lse}, bf16 ? 16 : 4));
+  const Sizes z = sizes(s, bf16 ? 2 : 4);
+  return fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}},
+                         {{o, z.tensor}, {lse, z.rows}});
+}
+
+fa_status check_bwd(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, const void* dq, const void* dk,
+                    const void* dv, const void* ws, size_t ws_bytes, const Shape& s,
+                    float scale, bool bf16) {
+  FA_TRY(fa::check_shape(s, bf16));
+  FA_TRY(fa::check_scale(scale));
+  if (s.empty()) return FA_OK;
+  const size_t al = bf16 ? 16 : 4;
+  FA_TRY(fa::check_ptrs({q, k, v, o, dO, dq, dk, dv}, al));
+  FA_TRY(fa::check_ptrs({lse}, bf16 ? 16 : 4));
+  FA_TRY(fa::check_workspace(ws, ws_bytes, fa::bwd_workspace_bytes(s, bf16)));
+  const Sizes z = sizes(s, bf16 ? 2 : 4);
+  const size_t wsz = fa::bwd_workspace_bytes(s, bf16);
+  return fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {o, z.tensor},
+                          {lse, z.rows}, {dO, z.tensor}},
+                         {{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {ws, wsz}});
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size or size too large";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim not supported (bf16: 64 or 128; fp32: 1..128)";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointer not aligned (bf16 path: 16 bytes; fp32 path: 4 bytes)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than required";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                 int64_t H, int64_t N, int64_t d, float scale, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_fwd(q, k, v, o, lse, s, scale, true));
+  if (s.empty()) return FA_OK;
+  return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return fa::bwd_workspace_bytes(Shape{B, H, N, d}, true);
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta, int64_t B, int64_t H,
+                            int64_t N, int64_t d, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  if (s.empty()) return FA_OK;
+  FA_TRY(fa::check_ptrs({o, dO, delta}, 16));
+  const Sizes z = sizes(s, 2);
+  FA_TRY(fa::check_alias({{o, z.tensor}, {dO, z.tensor}}, {{delta, z.rows}}));
+  return from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, as_stream(stream)));
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dO, const float* delta, void* dk, void* dv, int64_t B,
+                      int64_t H, int64_t N, int64_t d, float scale, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  FA_TRY(fa::check_scale(scale));
+  if (s.empty()) return FA_OK;
+  FA_TRY(fa::check_ptrs({q, k, v, lse, dO, delta, dk, dv}, 16));
+  const Sizes z = sizes(s, 2);
+  FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {lse, z.rows},
+                          {dO, z.tensor}, {delta, z.rows}},
+                         {{dk, z.tensor}, {dv, z.tensor}}));
+  return from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale,
+                                           as_stream(stream)));
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dO, const float* delta, void* dq, int64_t B, int64_t H,
+                    int64_t N, int64_t d, float scale, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  FA_TRY(fa::check_scale(scale));
+  if (s.empty()) return FA_OK;
+  FA_TRY(fa::check_ptrs({q, k, v, lse, dO, delta, dq}, 16));
+  const Sizes z = sizes(s, 2);
+  FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {lse, z.rows},
+                          {dO, z.tensor}, {delta, z.rows}},
+                         {{dq, z.tensor}}));
+  return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale,
+                                         as_stream(stream)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                 float scale, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, s, scale, true));
+  if (s.empty()) return FA_OK;
+  float* delta = static_cast<float*>(workspace);
+  hipStream_t st = as_stream(stream);
+  FA_TRY(from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, st)));
+  FA_TRY(from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, st)));
+  return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale, st));
+}
+
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_fwd(q, k, v, o, lse, s, scale, false));
+  if (s.empty()) return FA_OK;
+  return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
+}
+
+size_t fa_bwd_f32_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return fa::bwd_workspace_bytes(Shape{B, H, N, d}, false);
+}
+
+fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                     const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                     int64_t d, float scale, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, s, scale, false));
+  if (s.empty()) return FA_OK;
+  return from_hip(fa::launch_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv,
+                                     static_cast<float*>(workspace), B * H, N, d, scale,
+                                     as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// fp32 attention kernels: plain FMA arithmetic, natural exp, 8-query by 8-key
+// tiles, one wave per workgroup.  They follow the tiled recurrence with the
+// blocks of the fable of the 64 merchants (算珠楼的掌簿人, fable section 二: 64
+// rows cut into 8 stacks of 8) and serve tight checks at small sizes; the
+// bf16 kernels are the fast path.
+//
+// Forward, per query row (账房先生的奔命, section 六; rescale identity of the
+// star-observatory fable page, section "兩大核心魔法"):
+//   m' = max(m, rowmax S_b);  a = exp(m - m');  p = exp(S_b - m')
+//   l  = a l + rowsum p;      U = a U + p V_b;  m = m'
+// then O = U / l and LSE = m + ln l.
+// Backward (账房先生的奔命, section 七: P recomputed from Q, K and LSE):
+//   P = exp(s q.k - LSE),  dP = dO V^T,  dS = P (dP - D),  D = rowsum(dO * O)
+//   dV = P^T dO,  dK = s dS^T Q,  dQ = s dS K.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace fa {
+namespace {
+
+constexpr int T = 8;        // rows per tile (queries and keys)
+constexpr int DMAX = 128;   // largest head dim of the fp32 path
+constexpr int CPT = DMAX / T;  // columns per thread
+
+// Loads rows [r0, r0+T) of a [N][d] matrix into a [T][DMAX] LDS tile; rows at
+// or past N are zero.
+__device__ __forceinline__ void load_tile(float (*dst)[DMAX], const float* src, int r0, int N,
+                                          int d) {
+  for (int idx = threadIdx.x; idx < T * d; idx += 64) {
+    const int r = idx / d, c = idx - (idx / d) * d;
+    dst[r][c] = (r0 + r < N) ? src[(int64_t)(r0 + r) * d + c] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  return fmaxf(x, __shfl_xor(x, 4));
+}
+
+__device__ __forceinline__ float group8_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x + __shfl_xor(x, 4);
+}
+
+__device__ __forceinline__ float dot_rows(const float* a, const float* b, int d) {
+  float s = 0.0f;
+  for (int c = 0; c < d; ++c) s = fmaf(a[c], b[c], s);
+  return s;
+}
+
+// grid: (ceil(N/8) * B*H); block: 64.  Lane t: query r = t/8, key j = t%8 for
+// the scores; output columns c = t%8 + 8u of query r.
+__global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q,
+                                                     const float* __restrict__ k,
+                                                     const float* __restrict__ v,
+                                                     float* __restrict__ o,
+                                                     float* __restrict__ lse, int N, int d,
+                                                     int ntq, float scale) {
+  __shared__ float Qs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  const int bh = blockIdx.x / ntq, qt = blockIdx.x - bh * ntq;
+  const int64_t base = (int64_t)bh * N * d;
+  const int t = threadIdx.x, r = t >> 3, j = t & 7;
+  const int q0 = qt * T;
+  load_tile(Qs, q + base, q0, N, d);
+  float m = -INFINITY, l = 0.0f;
+  float acc[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) acc[u] = 0.0f;
+  const int nkt = (N + T - 1) / T;
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    load_tile(Ks, k + base, kt * T, N, d);
+    load_tile(Vs, v + base, kt * T, N, d);
+    __syncthreads();
+    float s = scale * dot_rows(Qs[r], Ks[j], d);
+    if (kt * T + j >= N) s = -INFINITY;
+    const float m_new = fmaxf(m, group8_max(s));
+    const float alpha = expf(m - m_new);  // exp(-inf) = 0 on the first block
+    const float p = expf(s - m_new);
+    l = alpha * l + group8_sum(p);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) acc[u] *= alpha;
+    for (int jj = 0; jj < T; ++jj) {
+      const float pj = __shfl(p, r * T + jj);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = j + T * u;
+        if (c < d) acc[u] = fmaf(pj, Vs[jj][c], acc[u]);
+      }
+    }
+    m = m_new;
+  }
+  const int qi = q0 + r;
+  if (qi < N) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = j + T * u;
+      if (c < d) o[base + (int64_t)qi * d + c] = acc[u] * inv;
+    }
+    if (j == 0) lse[(int64_t)bh * N + qi] = m + logf(l);
+  }
+}
+
+// D_i = sum_c dO_ic O_ic; one thread per row.
+__global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restrict__ o,
+                                                          const float* __restrict__ dO,
+                                                          float* __restrict__ delta,
+                                                          int64_t rows, int d) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  delta[row] = dot_rows(o + row * d, dO + row * d, d);
+}
+
+// Loads per-query LSE and D for rows [q0, q0+T); rows past N get LSE = +inf
+// (so P = 0) and D = 0.
+__device__ __forceinline__ void load_row_stats(float* lse_s, float* d_s, const float* lse,
+                                               const float* delta, int q0, int N) {
+  const int t = threadIdx.x;
+  if (t < T) {
+    const bool ok = q0 + t < N;
+    lse_s[t] = ok ? lse[q0 + t] : INFINITY;
+    d_s[t] = ok ? delta[q0 + t] : 0.0f;
+  }
+}
+
+// grid: (ceil(N/8) * B*H); block 64.  Workgroup owns keys [k0, k0+8).
+// Lane t: key j = t/8, query i = t%8 for the scores; accumulates dK, dV of
+// key j for columns c = t%8 + 8u.
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ lse, const float* __restrict__ dO,
+    const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv, int N,
+    int d, int nkt, float scale) {
+  __shared__ float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  __shared__ float lse_s[T], d_s[T];
+  const int bh = blockIdx.x / nkt, kt = blockIdx.x - bh * nkt;
+  const int64_t base = (int64_t)bh * N * d;
+  const float* lse_h = lse + (int64_t)bh * N;
+  const float* delta_h = delta + (int64_t)bh * N;
+  const int t = threadIdx.x, j = t >> 3, i = t & 7;
+  const int k0 = kt * T;
+  load_tile(Ks, k + base, k0, N, d);
+  load_tile(Vs, v + base, k0, N, d);
+  float accK[CPT], accV[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) accK[u] = accV[u] = 0.0f;
+  const int nqt = (N + T - 1) / T;
+  for (int qt = 0; qt < nqt; ++qt) {
+    __syncthreads();
+    load_tile(Qs, q + base, qt * T, N, d);
+    load_tile(dOs, dO + base, qt * T, N, d);
+    load_row_stats(lse_s, d_s, lse_h, delta_h, qt * T, N);
+    __syncthreads();
+    const float s = scale * dot_rows(Qs[i], Ks[j], d);
+    const float p = expf(s - lse_s[i]);
+    const float dp = dot_rows(dOs[i], Vs[j], d);
+    const float ds = p * (dp - d_s[i]);
+    for (int ii = 0; ii < T; ++ii) {
+      const float pi = __shfl(p, j * T + ii);
+      const float dsi = __shfl(ds, j * T + ii);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = i + T * u;
+        if (c < d) {
+          accV[u] = fmaf(pi, dOs[ii][c], accV[u]);
+          accK[u] = fmaf(dsi, Qs[ii][c], accK[u]);
+        }
+      }
+    }
+  }
+  const int kj = k0 + j;
+  if (kj < N) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = i + T * u;
+      if (c < d) {
+        dk[base + (int64_t)kj * d + c] = scale * accK[u];
+        dv[base + (int64_t)kj * d + c] = accV[u];
+      }
+    }
+  }
+}
+
+// grid: (ceil(N/8) * B*H); block 64.  Workgroup owns queries [q0, q0+8).
+// Lane t: query i = t/8, key j = t%8; accumulates dQ of query i for columns
+// c = t%8 + 8u.
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ lse, const float* __restrict__ dO,
+    const float* __restrict__ delta, float* __restrict__ dq, int N, int d, int nqt,
+    float scale) {
+  __shared__ float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  __shared__ float lse_s[T], d_s[T];
+  const int bh = blockIdx.x / nqt, qt = blockIdx.x - bh * nqt;
+  const int64_t base = (int64_t)bh * N * d;
+  const int t = threadIdx.x, i = t >> 3, j = t & 7;
+  const int q0 = qt * T;
+  load_tile(Qs, q + base, q0, N, d);
+  load_tile(dOs, dO + base, q0, N, d);
+  load_row_stats(lse_s, d_s, lse + (int64_t)bh * N, delta + (int64_t)bh * N, q0, N);
+  float acc[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) acc[u] = 0.0f;
+  const int nkt = (N + T - 1) / T;
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    load_tile(Ks, k + base, kt * T, N, d);
+    load_tile(Vs, v + base, kt * T, N, d);
+    __syncthreads();
+    const float s = scale * dot_rows(Qs[i], Ks[j], d);
+    const float p = (kt * T + j < N) ? expf(s - lse_s[i]) : 0.0f;
+    const float dp = dot_rows(dOs[i], Vs[j], d);
+    const float ds = p * (dp - d_s[i]);
+    for (int jj = 0; jj < T; ++jj) {
+      const float dsj = __shfl(ds, i * T + jj);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = j + T * u;
+        if (c < d) acc[u] = fmaf(dsj, Ks[jj][c], acc[u]);
+      }
+    }
+  }
+  const int qi = q0 + i;
+  if (qi < N) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = j + T * u;
+      if (c < d) dq[base + (int64_t)qi * d + c] = scale * acc[u];
+    }
+  }
+}
+
+}  // namespace
+
+int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
+  const int ntq = (int)((N + T - 1) / T);
+  hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)(ntq * BH)), dim3(64), 0, stream, q, k, v,
+                     o, lse, (int)N, (int)d, ntq, scale);
+  return (int)hipGetLastError();
+}
+
+int launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                   const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                   float* delta, int64_t BH, int64_t N, int64_t d, float scale,
+                   hipStream_t stream) {
+  const int64_t rows = BH * N;
+  hipLaunchKernelGGL(bwd_pre_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     stream, o, dO, delta, rows, (int)d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  const int nt = (int)((N + T - 1) / T);
+  hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k,
+                     v, lse, dO, delta, dk, dv, (int)N, (int)d, nt, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k, v,
+                     lse, dO, delta, dq, (int)N, (int)d, nt, scale);
+  return (int)hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,302 @@
+// bf16 attention forward for gfx950: one fused kernel, matrix cores for the
+// two contractions, online softmax in registers.
+//
+// Method (page tags: 账房先生的奔命 = carrie-l.github.io; star-observatory
+// fable = ckw19810413.github.io; 算珠楼的掌簿人 = hespethorn.github.io):
+//   Q is cut into row tiles and K, V into key tiles (账房先生的奔命, section 六,
+//   "Tiling").  For each key tile the scores S = Q K_j^T live only in
+//   registers; the running max m, running sum l and the unnormalised output
+//   U are updated with the rescale factor 2^(m_old - m_new) (the identity
+//   e^{x-m_new} = e^{x-m_old} e^{m_old-m_new} of the star-observatory fable,
+//   section "兩大核心魔法"), and at the end O = U / l and LSE = m + ln l are
+//   the only values written back (算珠楼的掌簿人, 技术解读).
+//
+// Work decomposition:
+//   workgroup = 128 query rows of one (batch, head); 4 waves x 32 rows.
+//   key tiles of 64 rows stream through LDS, double-buffered: the global
+//   loads of tile j+1 are issued before the math on tile j and written to
+//   the other LDS buffer after it, one barrier per tile.
+//   Scores are formed transposed, S^T = K Q^T, so that each lane owns one
+//   query row: lane l holds query l%32 for 16 of every 32 keys (the other 16
+//   sit in lane l^32).  The row max and row sum are in-lane reductions plus
+//   one exchange between the two half-waves.  The probabilities leave the
+//   score accumulators already in the B-operand layout of O^T += V^T P^T, so
+//   P never touches LDS; V is written to LDS transposed, with the keys of
+//   each 16-key step permuted to match (see kperm16).
+//   Base-2 domain: c = scale * log2(e); p = 2^(c s - m) with m in log2 units;
+//   LSE = ln 2 * (m + log2 l).
+#include "device_common.h"
+
+namespace fa {
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BR = 128;           // query rows per workgroup
+  static constexpr int BC = 64;            // key rows per tile
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int KP = D + 8;         // K tile row pitch in LDS (bf16), +16 B pad
+  static constexpr int VP = BC + 8;        // V^T tile row pitch in LDS (bf16), +16 B pad
+  static constexpr int K_ELEMS = BC * KP;
+  static constexpr int V_ELEMS = D * VP;
+  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
+  static constexpr int KCH = BC * D / 8;               // 16-byte chunks of a K tile
+  static constexpr int KCH_PER_T = (KCH + THREADS - 1) / THREADS;
+  static constexpr int VBLK = (BC / 4) * (D / 8);       // 4-row x 8-col blocks of a V tile
+  static constexpr int VBLK_PER_T = (VBLK + THREADS - 1) / THREADS;
+  static constexpr int DK = D / 16;                     // k-steps of the QK^T contraction
+  static constexpr int DB = D / 32;                     // 32-column blocks of O
+};
+
+// Maps the hardware workgroup id to a logical tile id so that consecutive
+// logical ids (the row tiles of one head) run on the same XCD: workgroups are
+// dealt to the 8 XCDs round-robin, and each XCD has its own L2, so the K/V
+// tiles of a head are then fetched into one L2 and reused there.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+  const int x = wg & 7, idx = wg >> 3;
+  const int base = nwg >> 3, rem = nwg & 7;
+  return x * base + (x < rem ? x : rem) + idx;
+}
+
+template <int D>
+struct TileRegs {
+  u32x4 k[FwdCfg<D>::KCH_PER_T];
+  u32x4 v[FwdCfg<D>::VBLK_PER_T][4];
+};
+
+// Global -> registers for key tile starting at row r0 (rows >= N read as 0).
+template <int D>
+__device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, const uint16_t* __restrict__ kh,
+                                             const uint16_t* __restrict__ vh, int r0, int N,
+                                             int tid) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::KCH_PER_T; ++u) {
+    const int cid = tid + u * C::THREADS;
+    const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if ((C::KCH % C::THREADS == 0 || cid < C::KCH) && r0 + row < N)
+      val = *reinterpret_cast<const u32x4*>(kh + (int64_t)(r0 + row) * D + col);
+    t.k[u] = val;
+  }
+#pragma unroll
+  for (int u = 0; u < C::VBLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    const int kq = b / (D / 8), col = (b % (D / 8)) * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if ((C::VBLK % C::THREADS == 0 || b < C::VBLK) && r0 + kq * 4 + r < N)
+        val = *reinterpret_cast<const u32x4*>(vh + (int64_t)(r0 + kq * 4 + r) * D + col);
+      t.v[u][r] = val;
+    }
+  }
+}
+
+// Registers -> LDS: K row-major [BC][KP]; V transposed and key-permuted
+// [D][VP] (row c holds column c of V for the tile's keys).
+template <int D>
+__device__ __forceinline__ void store_kv_tile(const TileRegs<D>& t, uint16_t* ks, uint16_t* vt,
+                                              int tid) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::KCH_PER_T; ++u) {
+    const int cid = tid + u * C::THREADS;
+    if (C::KCH % C::THREADS == 0 || cid < C::KCH) {
+      const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(ks + row * C::KP + col) = t.k[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C::VBLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {
+      const int kq = b / (D / 8), col = (b % (D / 8)) * 8;
+      const int key = kq * 4;                              // multiple of 4
+      const int pos = (key & ~15) + kperm16(key & 15);     // 4 contiguous slots
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int w = c >> 1;
+        uint32_t lo, hi;
+        if (c & 1) {
+          lo = (t.v[u][0][w] >> 16) | (t.v[u][1][w] & 0xffff0000u);
+          hi = (t.v[u][2][w] >> 16) | (t.v[u][3][w] & 0xffff0000u);
+        } else {
+          lo = (t.v[u][0][w] & 0xffffu) | (t.v[u][1][w] << 16);
+          hi = (t.v[u][2][w] & 0xffffu) | (t.v[u][3][w] << 16);
+        }
+        u32x2 pr = {lo, hi};
+        *reinterpret_cast<u32x2*>(vt + (col + c) * C::VP + pos) = pr;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int N,
+    int ntq, float c2) {
+  using C = FwdCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / ntq, qt = logical - bh * ntq;
+  const int64_t hoff = (int64_t)bh * N * D;
+  const uint16_t* qh = q + hoff;
+  const uint16_t* kh = k + hoff;
+  const uint16_t* vh = v + hoff;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, g = lane >> 5;
+  const int qrow = qt * C::BR + wave * 32 + li;   // this lane's query row
+
+  // Q^T as B operands, held for the whole loop: k-step kk covers columns
+  // kk*16 + 8g .. +7 of this lane's query row.
+  bf16x8 qreg[C::DK];
+#pragma unroll
+  for (int kk = 0; kk < C::DK; ++kk) {
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (qrow < N) val = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + kk * 16 + g * 8);
+    qreg[kk] = as_bf16x8(val);
+  }
+
+  f32x16 acc[C::DB];   // O^T blocks: rows = columns of O, col = this lane's query
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
+  float m_run = -INFINITY;   // running max of c*s, log2 units
+  float l_run = 0.0f;        // this lane's share of the running sum
+
+  const int nkt = (N + C::BC - 1) / C::BC;
+  TileRegs<D> tr;
+  load_kv_tile<D>(tr, kh, vh, 0, N, tid);
+  store_kv_tile<D>(tr, smem, smem + C::K_ELEMS, tid);
+  __syncthreads();
+
+  for (int j = 0; j < nkt; ++j) {
+    uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
+    uint16_t* vt = ks + C::K_ELEMS;
+    const bool more = j + 1 < nkt;
+    if (more) load_kv_tile<D>(tr, kh, vh, (j + 1) * C::BC, N, tid);
+
+    // S^T = K_j Q^T: two 32-key blocks; A = K rows from LDS, B = Q^T.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < C::DK; ++kk) {
+        const bf16x8 a = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(ks + (kb * 32 + li) * C::KP + kk * 16 + g * 8));
+        s[kb] = mfma32(a, qreg[kk], s[kb]);
+      }
+    }
+    // Keys past N in the last tile do not exist: their scores are -inf.
+    if (j * C::BC + C::BC > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j * C::BC + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= N) s[kb][i] = -INFINITY;
+        }
+    }
+    // Online softmax for this lane's query row.
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_across_halves(mx);
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float alpha = fast_exp2(m_run - m_new);
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[kb][i], c2, -m_new));
+        s[kb][i] = p;
+        rs += p;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+
+    // O^T += V_j^T P^T in 16-key steps; the B operand comes straight from the
+    // score accumulators (elements 8h..8h+7 of block kb hold the step's keys).
+#pragma unroll
+    for (int t = 0; t < C::BC / 16; ++t) {
+      const int kb = t >> 1, h = t & 1;
+      u32x4 pw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(s[kb][8 * h + 2 * e], s[kb][8 * h + 2 * e + 1]);
+      const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const bf16x8 a = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(vt + (db * 32 + li) * C::VP + t * 16 + g * 8));
+        acc[db] = mfma32(a, pb, acc[db]);
+      }
+    }
+
+    if (more) store_kv_tile<D>(tr, smem + ((j + 1) & 1) * C::BUF_ELEMS,
+                               smem + ((j + 1) & 1) * C::BUF_ELEMS + C::K_ELEMS, tid);
+    __syncthreads();
+  }
+
+  // Epilogue: O = U / l, LSE = ln2 * (m + log2 l).
+  const float l_tot = sum_across_halves(l_run);
+  if (qrow < N) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = o + hoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * r + 0] * inv, acc[db][4 * r + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * g) = w;
+      }
+    if (g == 0) lse[(int64_t)bh * N + qrow] = kLn2 * (m_run + log2f(l_tot));
+  }
+}
+
+template <int D>
+int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+           int64_t BH, int64_t N, float scale, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int ntq = (int)((N + C::BR - 1) / C::BR);
+  const int64_t nwg = (int64_t)ntq * BH;
+  static bool attr_set = false;  // idempotent; a race only repeats the call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return (int)e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)nwg), dim3(C::THREADS), C::LDS_BYTES,
+                     stream, q, k, v, o, lse, (int)N, ntq, scale * kLog2e);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* k16 = static_cast<const uint16_t*>(k);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  auto* o16 = static_cast<uint16_t*>(o);
+  if (d == 128) return launch<128>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+  return launch<64>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, the
+// bf16 matrix-core instruction, and small load/convert utilities.
+//
+// Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, one wave of
+// 64 lanes; l = lane, g = l / 32):
+//   A operand (32 x 16, row r, k):  lane l holds row r = l % 32, the 8 values
+//                                   of its k-group g.
+//   B operand (16 x 32, k, col c):  lane l holds col c = l % 32, the 8 values
+//                                   of its k-group g.
+//   C/D (32 x 32 fp32):             lane l, element i (0..15) holds
+//                                   row 8*(i/4) + 4*g + (i%4), col l % 32.
+// Because A and B use the same lane/k-group convention, a contraction is
+// correct whenever both operands enumerate the same k indices in the same
+// (group, element) order; the hardware's internal order of k does not matter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Round-to-nearest-even fp32 -> bf16 pair (lowered to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 p;
+  p[0] = static_cast<__bf16>(a);
+  p[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max over the two lanes that share l % 32 (lanes l and l ^ 32).
+__device__ __forceinline__ float max_across_halves(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+// Position of key k (0..15) inside a 16-key group of a "k-permuted" LDS row.
+// An accumulator lane of k-group g holds, for one 16-row step, the rows
+// {4g..4g+3, 8+4g..8+4g+3}; storing key k at position 8*g + 4*(k/8) + k%4
+// (g = (k/4)%2) makes those 8 keys contiguous, so the matching operand is one
+// 16-byte LDS read.
+__device__ __forceinline__ int kperm16(int k) {
+  return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
+}
+
+}  // namespace fa

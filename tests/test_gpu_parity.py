@@ -1,0 +1,319 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle
+on the same seeded inputs.
+
+Tolerances (see _compare.py): fp32 path max-abs 1e-5; bf16 path O max-abs
+1e-2 and mean-abs 1e-3, LSE max-abs 1e-3; gradients relative Frobenius 2e-2
+(bf16) and 1e-5 (fp32).  Several bf16 results are correct (rounding order of
+P, dS and the outputs), so bf16 parity is tolerance-based; integer/bitwise
+claims (determinism, exact zeros) are checked bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_softmax_02_amd as fa
+import oracle
+import synth
+from _compare import (TOL_BF16_GRAD_REL, TOL_BF16_LSE_MAX, TOL_BF16_O_MAX, TOL_BF16_O_MEAN,
+                      TOL_F32, TOL_F32_GRAD_REL, max_abs, mean_abs, rel_frobenius)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu(t):
+    return None if t is None else t.to(DEV)
+
+
+def f64(t):
+    return synth.to_f64(t)
+
+
+_ORACLE_CACHE = {}
+
+
+def oracle_fwd(name, q, k, v, scale, heads=None):
+    key = ("fwd", name, None if heads is None else tuple(heads))
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = oracle.sdpa_forward(f64(q), f64(k), f64(v), scale, heads=heads)
+    return _ORACLE_CACHE[key]
+
+
+def check_fwd_bf16(O, L, Oref, Lref, label):
+    o, l = f64(O), f64(L)
+    ma, mn, ml = max_abs(o, Oref), mean_abs(o, Oref), max_abs(l, Lref)
+    say(f"{label}: O max-abs {ma:.3e} mean-abs {mn:.3e}  LSE max-abs {ml:.3e}")
+    assert ma <= TOL_BF16_O_MAX and mn <= TOL_BF16_O_MEAN and ml <= TOL_BF16_LSE_MAX
+
+
+def grad_err(x, ref):
+    """Relative Frobenius error; an all-zero reference must be matched within
+    1e-6 absolute instead."""
+    if np.linalg.norm(ref) == 0.0:
+        return 0.0 if max_abs(x, ref) <= 1e-6 else float("inf")
+    return rel_frobenius(x, ref)
+
+
+# ---------------------------------------------------------------------------
+# fp32 path
+# ---------------------------------------------------------------------------
+
+def test_tiny_f32_forward():
+    w = synth.WORKLOADS["tiny_f32_n64_d64"]
+    say(f"case {w.name}")
+    q, k, v, _ = synth.make_inputs(w)
+    O, L = fa.fa_fwd_f32(gpu(q), gpu(k), gpu(v), w.scale)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), w.scale)
+    ea, el = max_abs(f64(O), Oref), max_abs(f64(L), Lref)
+    say(f"  O max-abs {ea:.2e}  LSE max-abs {el:.2e}")
+    assert ea <= TOL_F32 and el <= TOL_F32
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 1), (1, 2, 7, 3), (2, 1, 65, 64),
+                                     (1, 1, 100, 128), (1, 3, 33, 17), (1, 1, 9, 8)])
+def test_f32_forward_shapes(B, H, N, d):
+    say(f"case f32 fwd B={B} H={H} N={N} d={d}")
+    q, k, v, _ = synth.make_qkv(B, H, N, d, torch.float32, seed=100 + N + d)
+    s = synth.default_scale(d)
+    O, L = fa.fa_fwd_f32(gpu(q), gpu(k), gpu(v), s)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
+    assert max_abs(f64(O), Oref) <= TOL_F32
+    assert max_abs(f64(L), Lref) <= TOL_F32
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 64, 64), (1, 2, 37, 16), (2, 1, 8, 4),
+                                     (1, 1, 1, 8), (1, 1, 17, 128)])
+def test_f32_backward(B, H, N, d):
+    say(f"case f32 bwd B={B} H={H} N={N} d={d}")
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.float32, seed=200 + N + d, backward=True)
+    s = synth.default_scale(d)
+    qg, kg, vg, gg = gpu(q), gpu(k), gpu(v), gpu(dO)
+    O, L = fa.fa_fwd_f32(qg, kg, vg, s)
+    dq, dk, dv = fa.fa_bwd_f32(qg, kg, vg, O, L, gg, s)
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = grad_err(f64(x), ref)
+        say(f"  {name} rel-Frobenius {e:.2e}")
+        assert e <= TOL_F32_GRAD_REL, name
+
+
+# ---------------------------------------------------------------------------
+# bf16 path: workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["fwd_bf16_b4h16_n2048_d64", "long_bf16_b1h16_n8192_d128",
+                                  "long_bf16_b1h16_n8192_d128_outlier",
+                                  "fwdbwd_bf16_b2h16_n4096_d128"])
+def test_bf16_forward_workload(name):
+    w = synth.WORKLOADS[name]
+    say(f"case {name}")
+    q, k, v, _ = synth.make_inputs(w, backward=False)
+    O, L = fa.fa_fwd(gpu(q), gpu(k), gpu(v), w.scale)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle_fwd(name, q, k, v, w.scale)
+    check_fwd_bf16(O, L, Oref, Lref, name)
+
+
+def test_vlong_forward_sampled_rows_and_memory():
+    w = synth.WORKLOADS["vlong_bf16_b1h8_n131072_d128"]
+    say(f"case {w.name}")
+    q, k, v, _ = synth.make_inputs(w)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    warm = qg[:, :1, :256].contiguous()
+    fa.fa_fwd(warm, warm, warm, w.scale)      # code objects loaded before measuring
+    o = torch.empty_like(qg)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    free0 = torch.cuda.mem_get_info()[0]
+    fa.fa_fwd(qg, kg, vg, w.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    peak = torch.cuda.max_memory_allocated()
+    io_bytes = 4 * q.numel() * 2 + lse.numel() * 4
+    say(f"  peak allocated {peak / 1e9:.3f} GB; inputs+outputs {io_bytes / 1e9:.3f} GB; "
+        f"free-memory change {free0 - free1} B")
+    assert peak == base                      # the call allocates nothing through torch
+    assert peak <= 1.1 * io_bytes
+    assert free0 - free1 <= 2 * 1024 * 1024   # and no hidden device allocation
+    rows = synth.sampled_rows(w)
+    Oh, Lh = f64(o).reshape(w.B * w.H, w.N, w.d), f64(lse).reshape(w.B * w.H, w.N)
+    qf, kf, vf = (f64(x).reshape(w.B * w.H, w.N, w.d) for x in (q, k, v))
+    worst = [0.0, 0.0, 0.0]
+    for bh in range(w.B * w.H):
+        r = rows[bh]
+        Oref, Lref = oracle.sdpa_rows(qf[bh][r], kf[bh], vf[bh], w.scale)
+        worst[0] = max(worst[0], max_abs(Oh[bh][r], Oref))
+        worst[1] = max(worst[1], mean_abs(Oh[bh][r], Oref))
+        worst[2] = max(worst[2], max_abs(Lh[bh][r], Lref))
+    say(f"  sampled rows: O max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} "
+        f"LSE max-abs {worst[2]:.3e}")
+    assert worst[0] <= TOL_BF16_O_MAX and worst[1] <= TOL_BF16_O_MEAN
+    assert worst[2] <= TOL_BF16_LSE_MAX
+
+
+def run_bf16_fwd_bwd(q, k, v, dO, scale):
+    qg, kg, vg, gg = gpu(q), gpu(k), gpu(v), gpu(dO)
+    O, L = fa.fa_fwd(qg, kg, vg, scale)
+    dq, dk, dv = fa.fa_bwd(qg, kg, vg, O, L, gg, scale)
+    torch.cuda.synchronize()
+    return O, L, dq, dk, dv
+
+
+def test_bf16_backward_workload():
+    w = synth.WORKLOADS["fwdbwd_bf16_b2h16_n4096_d128"]
+    say(f"case {w.name} backward")
+    q, k, v, dO = synth.make_inputs(w)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, w.scale)
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), w.scale)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = rel_frobenius(f64(x), ref)
+        say(f"  {name} rel-Frobenius {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+def test_bf16_backward_metric_shape_heads():
+    """B=1, H=16, N=8192, d=128: the GPU runs every head; heads 0 and 15 are
+    compared with the oracle (each head is independent)."""
+    w = synth.WORKLOADS["attn_bf16_b1h16_n8192_d128_fwdbwd"]
+    say(f"case {w.name} backward, heads 0 and 15")
+    q, k, v, dO = synth.make_inputs(w)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, w.scale)
+    heads = [0, 15]
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), w.scale, heads=heads)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        xh = f64(x)[0, heads]
+        e = rel_frobenius(xh, ref[0, heads])
+        say(f"  {name} rel-Frobenius {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+# ---------------------------------------------------------------------------
+# bf16 path: ragged sizes, special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 65, 130, 1000])
+def test_bf16_ragged_forward_backward(N, d):
+    say(f"case bf16 ragged N={N} d={d}")
+    B, H = 1, 2
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=300 + N + d, backward=True)
+    s = synth.default_scale(d)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, s)
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
+    check_fwd_bf16(O, L, Oref, Lref, f"  fwd N={N} d={d}")
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = grad_err(f64(x), ref)
+        say(f"  {name} err {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_q_zero(d):
+    """Q = 0: O is the column mean of V, LSE = ln N, dK is exactly zero and
+    every dV row is the mean of dO's rows."""
+    N = 300
+    say(f"case bf16 Q=0 d={d}")
+    _, k, v, dO = synth.make_qkv(1, 2, N, d, torch.bfloat16, seed=7, backward=True)
+    q = torch.zeros_like(k)
+    s = synth.default_scale(d)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, s)
+    vm = f64(v).mean(axis=2, keepdims=True)
+    assert max_abs(f64(O), vm) <= TOL_BF16_O_MAX
+    assert max_abs(f64(L), math.log(N)) <= TOL_BF16_LSE_MAX
+    assert torch.count_nonzero(dk).item() == 0
+    gm = np.broadcast_to(f64(dO).mean(axis=2, keepdims=True), dv.shape)
+    assert rel_frobenius(f64(dv), gm) <= TOL_BF16_GRAD_REL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_dominant_key(d):
+    """All queries e_0, one key 1024 e_0, other keys orthogonal to e_0: the
+    softmax puts (1 - ~N e^-delta) on that key, so O_i = V_j* and LSE_i =
+    S_ij* = 1024 * scale."""
+    N, jstar = 777, 613
+    say(f"case bf16 dominant key d={d}")
+    _, k, v, _ = synth.make_qkv(1, 1, N, d, torch.bfloat16, seed=11)
+    q = torch.zeros_like(k)
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[0, 0, jstar] = 0.0
+    k[0, 0, jstar, 0] = 1024.0
+    s = synth.default_scale(d)
+    O, L = fa.fa_fwd(gpu(q), gpu(k), gpu(v), s)
+    torch.cuda.synchronize()
+    assert max_abs(f64(O)[0, 0], f64(v)[0, 0, jstar][None, :]) <= TOL_BF16_O_MAX
+    assert max_abs(f64(L), 1024.0 * s) <= TOL_BF16_LSE_MAX
+
+
+def test_bf16_forward_is_deterministic():
+    w = synth.WORKLOADS["fwd_bf16_b4h16_n2048_d64"]
+    say("case bf16 forward determinism")
+    q, k, v = (gpu(x) for x in synth.make_inputs(w, backward=False)[:3])
+    O0, L0 = fa.fa_fwd(q, k, v, w.scale)
+    for _ in range(20):
+        O, L = fa.fa_fwd(q, k, v, w.scale)
+        assert torch.equal(O, O0) and torch.equal(L, L0)
+
+
+def test_bf16_backward_is_deterministic_and_stages_match():
+    say("case bf16 backward determinism and stage entry points")
+    q, k, v, dO = (gpu(x) for x in synth.make_qkv(1, 3, 1000, 128, torch.bfloat16, 21,
+                                                   backward=True))
+    s = synth.default_scale(128)
+    O, L = fa.fa_fwd(q, k, v, s)
+    ref = fa.fa_bwd(q, k, v, O, L, dO, s)
+    for _ in range(5):
+        out = fa.fa_bwd(q, k, v, O, L, dO, s)
+        assert all(torch.equal(a, b) for a, b in zip(out, ref))
+    delta = fa.fa_bwd_preprocess(O, dO)
+    dk, dv = fa.fa_bwd_dkdv(q, k, v, L, dO, delta, s)
+    dq = fa.fa_bwd_dq(q, k, v, L, dO, delta, s)
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+    # delta is rowsum(dO * O) of the stored bf16 O
+    dref = (dO.double() * O.double()).sum(-1)
+    assert (delta.double() - dref).abs().max().item() <= 1e-4
+
+
+def test_side_stream_and_empty_and_errors():
+    say("case streams, empty problems, error paths")
+    q, k, v = (gpu(x) for x in synth.make_qkv(1, 2, 256, 64, torch.bfloat16, 5)[:3])
+    s = synth.default_scale(64)
+    O0, L0 = fa.fa_fwd(q, k, v, s)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        O1, L1 = fa.fa_fwd(q, k, v, s)
+    side.synchronize()
+    assert torch.equal(O0, O1) and torch.equal(L0, L1)
+    # empty problem: nothing to do, no error
+    e = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    Oe, Le = fa.fa_fwd(e, e, e, s)
+    assert Oe.shape == e.shape and Le.shape == (1, 2, 0)
+    # misaligned: a view starting one element in
+    big = torch.zeros(1, 1, 1, 64 * 9, dtype=torch.bfloat16, device=DEV)
+    mis = big.view(-1)[1:1 + 8 * 64].view(1, 1, 8, 64)
+    with pytest.raises(fa.FAError, match="FA_ERR_ALIGN"):
+        fa.fa_fwd(mis, mis, mis, s)
+    # output aliasing an input
+    with pytest.raises(fa.FAError, match="FA_ERR_ALIAS"):
+        fa.fa_fwd(q, k, v, s, o=q)
+    # unsupported head dim on the bf16 path
+    x96 = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FAError, match="FA_ERR_UNSUPPORTED"):
+        fa.fa_fwd(x96, x96, x96)
+    torch.cuda.synchronize()
