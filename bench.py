@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 METRIC = "attention TFLOP/s fwd & fwd+bwd, % of bf16 MFMA peak, N=8192 d=128"
 WORKLOAD = "attn_bf16_b1h16_n8192_d128_fwdbwd"
+COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 
 
 def parse():
@@ -106,7 +107,16 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     delta = ws.view(torch.float32)[: B * H * N].view(B, H, N)
     stream = torch.cuda.current_stream(dev)
+    # A plain device copy of known size, outside the timed region: its
+    # FETCH_SIZE / WRITE_SIZE counters calibrate the traffic of the kernels.
+    cal_src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    ms_copy = time_launches(lambda: cal_dst.copy_(cal_src), 3, stream)
+    del cal_src, cal_dst
+
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
     mem_base = torch.cuda.memory_allocated()
 
@@ -192,6 +202,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "kernels": {kname: {"ms": round(kv["ms"], 4), "tflops": round(kv["tflops"], 2)}
                     for kname, kv in kernels.items()},
+        "hbm_copy_GBps": round(2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9, 1),
         "peak_mem_bytes": int(peak_mem),
         "mem_inputs_outputs_bytes": int(mem_base),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),

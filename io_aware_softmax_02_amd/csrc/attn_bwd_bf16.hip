@@ -67,10 +67,11 @@ __device__ __forceinline__ void load_block4x8(u32x4 (&r)[4], const uint16_t* __r
 }
 
 // Writes a loaded 4x8 block row-major into an LDS tile with pitch P, and
-// transposed + permuted into an LDS tile with pitch TP (row = column of the
-// source; within each 16-row step the source rows are placed by kperm16).
+// transposed + permuted into a swizzled 64-position tile (tswz; row = column
+// of the source; within each 16-row step the source rows are placed by
+// kperm16).
 __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* rowmajor, int P,
-                                               uint16_t* trans, int TP, int row0, int col) {
+                                               uint16_t* trans, int row0, int col) {
   if (rowmajor) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rowmajor + (row0 + i) * P + col) = r[i];
@@ -88,7 +89,7 @@ __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* ro
       hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
     }
     u32x2 pr = {lo, hi};
-    *reinterpret_cast<u32x2*>(trans + (col + c) * TP + pos) = pr;
+    *reinterpret_cast<u32x2*>(trans + tswz(col + c, pos)) = pr;
   }
 }
 
@@ -105,9 +106,8 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128, BQ = 64, THREADS = 256;
   static constexpr int P = D + 8;        // row-major tile pitch (bf16)
-  static constexpr int TP = BQ + 8;      // transposed tile pitch (bf16)
   static constexpr int ROW_ELEMS = BQ * P;
-  static constexpr int T_ELEMS = D * TP;
+  static constexpr int T_ELEMS = D * 64;  // transposed tiles (tswz layout)
   // LDS: Qs, dOs (row-major), Qt, dOt (transposed), lse2[BQ], delta[BQ]
   static constexpr int OFF_QS = 0;
   static constexpr int OFF_DOS = OFF_QS + ROW_ELEMS;
@@ -117,6 +117,7 @@ struct DkdvCfg {
   static constexpr int LDS_BYTES = OFF_STATS * 2 + 2 * BQ * 4;
   static constexpr int NBLK = (BQ / 4) * (D / 8);       // 4x8 blocks per tile matrix
   static constexpr int DK = D / 16, DB = D / 32;
+  static_assert(BQ == 64, "transposed tiles hold 64 positions per row");
 };
 
 template <int D>
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const int r0 = (bb / (D / 8)) * 4, col = (bb % (D / 8)) * 8;
       u32x4 r[4];
       load_block4x8<D>(r, (isq ? qh : doh), q0 + r0, col, N);
-      store_block4x8(r, isq ? Qs : dOs, C::P, isq ? Qt : dOt, C::TP, r0, col);
+      store_block4x8(r, isq ? Qs : dOs, C::P, isq ? Qt : dOt, r0, col);
     }
     if (tid < C::BQ) {
       const int qi = q0 + tid;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const bf16x8 pb = as_bf16x8(pw), sb = as_bf16x8(sw);
 #pragma unroll
       for (int cb = 0; cb < C::DB; ++cb) {
-        const int off = (cb * 32 + li) * C::TP + t * 16 + g * 8;
+        const int off = tswz(cb * 32 + li, t * 16 + g * 8);
         dvt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dOt + off)), pb, dvt[cb]);
         dkt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Qt + off)), sb, dkt[cb]);
       }
@@ -261,15 +262,15 @@ template <int D>
 struct DqCfg {
   static constexpr int BQ = 128, BK = 64, THREADS = 256;
   static constexpr int P = D + 8;
-  static constexpr int TP = BK + 8;
   static constexpr int ROW_ELEMS = BK * P;
-  static constexpr int T_ELEMS = D * TP;
+  static constexpr int T_ELEMS = D * 64;  // transposed tile (tswz layout)
   static constexpr int OFF_KS = 0;
   static constexpr int OFF_VS = OFF_KS + ROW_ELEMS;
   static constexpr int OFF_KT = OFF_VS + ROW_ELEMS;
   static constexpr int LDS_BYTES = (OFF_KT + T_ELEMS) * 2;
   static constexpr int NBLK = (BK / 4) * (D / 8);
   static constexpr int DK = D / 16, DB = D / 32;
+  static_assert(BK == 64, "transposed tiles hold 64 positions per row");
 };
 
 template <int D>
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       u32x4 r[4];
       load_block4x8<D>(r, isk ? kh : vh, k0 + r0, col, N);
       if (isk) {
-        store_block4x8(r, Ks, C::P, Kt, C::TP, r0, col);
+        store_block4x8(r, Ks, C::P, Kt, r0, col);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(Vs + (r0 + i) * C::P + col) = r[i];
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       const bf16x8 sb = as_bf16x8(sw);
 #pragma unroll
       for (int cb = 0; cb < C::DB; ++cb) {
-        const int off = (cb * 32 + li) * C::TP + t * 16 + g * 8;
+        const int off = tswz(cb * 32 + li, t * 16 + g * 8);
         dqt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + off)), sb, dqt[cb]);
       }
     }

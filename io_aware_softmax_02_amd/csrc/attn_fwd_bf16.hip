@@ -30,6 +30,9 @@
 namespace fa {
 namespace {
 
+// Slack of the lazily updated softmax reference, in log2 units.
+constexpr float kSlack = 8.0f;
+
 template <int D>
 struct FwdCfg {
   static constexpr int BR = 128;           // query rows per workgroup
@@ -84,7 +87,7 @@ __device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, const uint16_t* __r
 #pragma unroll
   for (int u = 0; u < C::VBLK_PER_T; ++u) {
     const int b = tid + u * C::THREADS;
-    const int kq = b / (D / 8), col = (b % (D / 8)) * 8;
+    const int kq = b % (C::BC / 4), col = (b / (C::BC / 4)) * 8;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       u32x4 val = {0u, 0u, 0u, 0u};
@@ -113,7 +116,7 @@ __device__ __forceinline__ void store_kv_tile(const TileRegs<D>& t, uint16_t* ks
   for (int u = 0; u < C::VBLK_PER_T; ++u) {
     const int b = tid + u * C::THREADS;
     if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {
-      const int kq = b / (D / 8), col = (b % (D / 8)) * 8;
+      const int kq = b % (C::BC / 4), col = (b / (C::BC / 4)) * 8;
       const int key = kq * 4;                              // multiple of 4
       const int pos = (key & ~15) + kperm16(key & 15);     // 4 contiguous slots
 #pragma unroll
@@ -204,45 +207,58 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           if (key >= N) s[kb][i] = -INFINITY;
         }
     }
-    // Online softmax for this lane's query row.
+    // Online softmax for this lane's query row.  The reference value m_run
+    // moves only when some row of the wave sees a score more than 2^kSlack
+    // above it; until then the factor 2^(m_old - m_new) would be 1 for the
+    // rows that did not grow and the rescale is skipped.  P~ = 2^(c s - m_run)
+    // then stays <= 2^kSlack, and because U and l share the same reference
+    // value the result O = U / l is unchanged (the rescale identity holds for
+    // any common reference, not only the running maximum).
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = max_across_halves(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = fast_exp2(m_run - m_new);
+    const float m_cand = mx * c2;
+    if (__any(m_cand > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    // P~ in fp32 for the row sum, rounded to bf16 (RNE) in the B-operand
+    // layout of the next contraction.
+    bf16x8 pb[C::BC / 16];
     float rs = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[kb][i], c2, -m_new));
-        s[kb][i] = p;
-        rs += p;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-
-    // O^T += V_j^T P^T in 16-key steps; the B operand comes straight from the
-    // score accumulators (elements 8h..8h+7 of block kb hold the step's keys).
 #pragma unroll
     for (int t = 0; t < C::BC / 16; ++t) {
       const int kb = t >> 1, h = t & 1;
       u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(s[kb][8 * h + 2 * e], s[kb][8 * h + 2 * e + 1]);
-      const bf16x8 pb = as_bf16x8(pw);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s[kb][8 * h + 2 * e], c2, -m_run));
+        const float p1 = fast_exp2(fmaf(s[kb][8 * h + 2 * e + 1], c2, -m_run));
+        rs += p0 + p1;
+        pw[e] = pack_bf16x2(p0, p1);
+      }
+      pb[t] = as_bf16x8(pw);
+    }
+    l_run += rs;
+
+    // O^T += V_j^T P^T in 16-key steps (elements 8h..8h+7 of score block kb
+    // hold the step's keys in the operand's k order).
+#pragma unroll
+    for (int t = 0; t < C::BC / 16; ++t) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
         const bf16x8 a = as_bf16x8(
             *reinterpret_cast<const u32x4*>(vt + (db * 32 + li) * C::VP + t * 16 + g * 8));
-        acc[db] = mfma32(a, pb, acc[db]);
+        acc[db] = mfma32(a, pb[t], acc[db]);
       }
     }
 

@@ -80,4 +80,14 @@ __device__ __forceinline__ int kperm16(int k) {
   return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
 }
 
+// Transposed LDS tile with 64 positions per row (128 B, no padding), its
+// 16-byte chunks XOR-swizzled by row: offset (in bf16 elements) of position
+// pos of row r.  Rows r..r+7 read at the same logical chunk land in 8
+// different bank groups, and so do rows 8 apart, so both the 8-byte writes of
+// a register transpose and the 16-byte operand reads are free of bank
+// conflicts.  pos must be a multiple of 4 (writes) or 8 (reads).
+__device__ __forceinline__ int tswz(int r, int pos) {
+  return r * 64 + (((pos >> 3) ^ ((r ^ (r >> 3)) & 7)) << 3) + (pos & 7);
+}
+
 }  // namespace fa
