@@ -63,9 +63,11 @@ const char* fa_status_str(fa_status s);
 
 /* ------------------------------------------------------------------------ */
 /* bf16 path: Q, K, V, O, dO, dQ, dK, dV hold bfloat16 (uint16 storage).    */
-/* Head dim d must be 64 or 128.  Tensor pointers 16-byte aligned; LSE and   */
-/* the workspace 16-byte aligned.  Accumulation is fp32 throughout; P and dS */
-/* are rounded to bf16 (round to nearest even) before their contractions.    */
+/* Head dim d must be 64 or 128, and one head of one tensor at most 2 GiB:  */
+/* (N + 128) * d * 2 < 2^31 bytes, else FA_ERR_SHAPE.  Tensor pointers, LSE  */
+/* and the workspace 16-byte aligned.  Accumulation is fp32 throughout; P    */
+/* and dS are rounded to bf16 (round to nearest even) before their           */
+/* contractions.                                                              */
 /* ------------------------------------------------------------------------ */
 
 /* Forward.  Inputs q, k, v; outputs o (bf16) and lse (fp32, natural log).

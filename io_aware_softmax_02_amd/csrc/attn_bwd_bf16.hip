@@ -13,9 +13,14 @@
 // Matrix-core layout as in device_common.h.  Each contraction keeps one
 // operand in registers and reads the other from LDS; an operand whose
 // contraction index runs along a tile's rows (Q^T in dK, dO^T in dV, K^T in
-// dQ) is stored transposed and key/query-permuted (kperm16) so that the
-// 8 values a lane needs are one 16-byte read and line up with the score
+// dQ) is stored transposed and key/query-permuted (kperm16, tswz) so that
+// the 8 values a lane needs are one 16-byte read and line up with the score
 // accumulator layout that supplies the other operand.
+//
+// Streaming: the tiles of the loop are fetched with buffer loads (reads past
+// the end of a head return 0, which is what a ragged last tile needs) into
+// registers one tile ahead, and written to the other half of a double-buffered
+// LDS area after the math on the current tile; one barrier per tile.
 #include "device_common.h"
 
 namespace fa {
@@ -54,42 +59,42 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (row < rows && tid % LPR == 0) delta[row] = s;
 }
 
-// Loads a 4-row x 8-column block of a [N][D] bf16 matrix (rows >= N are 0).
+// A tile of 64 rows x D columns is handled as 4-row x 8-column blocks; block
+// b covers rows 4*(b / (D/8)) .. +3 and columns 8*(b % (D/8)) .. +7 (consecutive
+// lanes along a row, so the row-major LDS writes are conflict-free).
 template <int D>
-__device__ __forceinline__ void load_block4x8(u32x4 (&r)[4], const uint16_t* __restrict__ src,
-                                              int row0, int col, int N) {
+__device__ __forceinline__ void load_block(u32x4 (&r)[4], rsrc_t src, int row0, int b) {
+  const int r0 = (b / (D / 8)) * 4, col = (b % (D / 8)) * 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row0 + i < N) val = *reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + i) * D + col);
-    r[i] = val;
-  }
+  for (int i = 0; i < 4; ++i) r[i] = buf_load16(src, (uint32_t)(((row0 + r0 + i) * D + col) * 2));
 }
 
-// Writes a loaded 4x8 block row-major into an LDS tile with pitch P, and
-// transposed + permuted into a swizzled 64-position tile (tswz; row = column
-// of the source; within each 16-row step the source rows are placed by
-// kperm16).
-__device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* rowmajor, int P,
-                                               uint16_t* trans, int row0, int col) {
+// Writes a loaded block row-major into an LDS tile with pitch P (if given) and
+// transposed + permuted into a swizzled 64-position tile (if given).
+template <int D>
+__device__ __forceinline__ void store_block(const u32x4 (&r)[4], int b, uint16_t* rowmajor, int P,
+                                            uint16_t* trans) {
+  const int r0 = (b / (D / 8)) * 4, col = (b % (D / 8)) * 8;
   if (rowmajor) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rowmajor + (row0 + i) * P + col) = r[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rowmajor + (r0 + i) * P + col) = r[i];
   }
-  const int pos = (row0 & ~15) + kperm16(row0 & 15);
+  if (trans) {
+    const int pos = (r0 & ~15) + kperm16(r0 & 15);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1;
-    uint32_t lo, hi;
-    if (c & 1) {
-      lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-      hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-    } else {
-      lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-      hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+    for (int c = 0; c < 8; ++c) {
+      const int w = c >> 1;
+      uint32_t lo, hi;
+      if (c & 1) {
+        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+      } else {
+        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+      }
+      u32x2 pr = {lo, hi};
+      *reinterpret_cast<u32x2*>(trans + tswz(col + c, pos)) = pr;
     }
-    u32x2 pr = {lo, hi};
-    *reinterpret_cast<u32x2*>(trans + tswz(col + c, pos)) = pr;
   }
 }
 
@@ -105,20 +110,64 @@ __device__ __forceinline__ void store_block4x8(const u32x4 (&r)[4], uint16_t* ro
 template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128, BQ = 64, THREADS = 256;
-  static constexpr int P = D + 8;        // row-major tile pitch (bf16)
+  static constexpr int P = D + 8;            // row-major tile pitch (bf16)
   static constexpr int ROW_ELEMS = BQ * P;
-  static constexpr int T_ELEMS = D * 64;  // transposed tiles (tswz layout)
-  // LDS: Qs, dOs (row-major), Qt, dOt (transposed), lse2[BQ], delta[BQ]
+  static constexpr int T_ELEMS = D * 64;     // transposed tiles (tswz layout)
+  // One buffer: Qs, dOs (row-major), Qt, dOt (transposed), lse2[BQ], delta[BQ]
   static constexpr int OFF_QS = 0;
   static constexpr int OFF_DOS = OFF_QS + ROW_ELEMS;
   static constexpr int OFF_QT = OFF_DOS + ROW_ELEMS;
   static constexpr int OFF_DOT = OFF_QT + T_ELEMS;
-  static constexpr int OFF_STATS = OFF_DOT + T_ELEMS;  // in bf16 units; floats follow
-  static constexpr int LDS_BYTES = OFF_STATS * 2 + 2 * BQ * 4;
-  static constexpr int NBLK = (BQ / 4) * (D / 8);       // 4x8 blocks per tile matrix
+  static constexpr int OFF_STATS = OFF_DOT + T_ELEMS;   // bf16 units; 2*BQ floats follow
+  static constexpr int BUF_ELEMS = OFF_STATS + 4 * BQ;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
+  static constexpr int NBLK = (BQ / 4) * (D / 8);         // blocks per matrix per tile
+  static constexpr int BLK_PER_T = 2 * NBLK / THREADS;   // Q and dO blocks per thread
   static constexpr int DK = D / 16, DB = D / 32;
   static_assert(BQ == 64, "transposed tiles hold 64 positions per row");
+  static_assert((2 * NBLK) % THREADS == 0, "whole blocks per thread");
 };
+
+template <int D>
+struct DkdvTile {
+  u32x4 blk[DkdvCfg<D>::BLK_PER_T][4];
+  float stat;
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_load(DkdvTile<D>& t, rsrc_t rq, rsrc_t rdo, rsrc_t rlse,
+                                          rsrc_t rdel, int q0, int tid) {
+  using C = DkdvCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::BLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    const bool isq = b < C::NBLK;
+    load_block<D>(t.blk[u], isq ? rq : rdo, q0, isq ? b : b - C::NBLK);
+  }
+  t.stat = 0.0f;
+  if (tid < 2 * C::BQ) t.stat = buf_loadf(tid < C::BQ ? rlse : rdel,
+                                         (uint32_t)((q0 + (tid & (C::BQ - 1))) * 4));
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_store(const DkdvTile<D>& t, uint16_t* buf, int q0, int N,
+                                           int tid) {
+  using C = DkdvCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::BLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    const bool isq = b < C::NBLK;
+    store_block<D>(t.blk[u], isq ? b : b - C::NBLK, buf + (isq ? C::OFF_QS : C::OFF_DOS), C::P,
+                   buf + (isq ? C::OFF_QT : C::OFF_DOT));
+  }
+  float* st = reinterpret_cast<float*>(buf + C::OFF_STATS);
+  if (tid < C::BQ) {
+    // log2-domain LSE; +inf past N makes P exactly 0 for rows that do not exist
+    st[tid] = q0 + tid < N ? t.stat * kLog2e : INFINITY;
+  } else if (tid < 2 * C::BQ) {
+    st[tid] = t.stat;    // delta, 0 past N
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
@@ -129,20 +178,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     float scale) {
   using C = DkdvCfg<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Qs = smem + C::OFF_QS;
-  uint16_t* dOs = smem + C::OFF_DOS;
-  uint16_t* Qt = smem + C::OFF_QT;
-  uint16_t* dOt = smem + C::OFF_DOT;
-  float* lse2s = reinterpret_cast<float*>(smem + C::OFF_STATS);
-  float* ds_ = lse2s + C::BQ;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nkt, kt = logical - bh * nkt;
   const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* qh = q + hoff;
-  const uint16_t* doh = dO + hoff;
-  const float* lseh = lse + (int64_t)bh * N;
-  const float* delh = delta + (int64_t)bh * N;
+  const uint32_t hbytes = (uint32_t)N * D * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes);
+  const rsrc_t rdo = make_rsrc(dO + hoff, hbytes);
+  const rsrc_t rk = make_rsrc(k + hoff, hbytes);
+  const rsrc_t rv = make_rsrc(v + hoff, hbytes);
+  const rsrc_t rlse = make_rsrc(lse + (int64_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t rdel = make_rsrc(delta + (int64_t)bh * N, (uint32_t)N * 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
@@ -152,36 +198,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   bf16x8 kreg[C::DK], vreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      a = *reinterpret_cast<const u32x4*>(k + hoff + (int64_t)key * D + kk * 16 + g * 8);
-      b = *reinterpret_cast<const u32x4*>(v + hoff + (int64_t)key * D + kk * 16 + g * 8);
-    }
-    kreg[kk] = as_bf16x8(a);
-    vreg[kk] = as_bf16x8(b);
+    const uint32_t off = (uint32_t)((key * D + kk * 16 + g * 8) * 2);
+    kreg[kk] = as_bf16x8(buf_load16(rk, off));
+    vreg[kk] = as_bf16x8(buf_load16(rv, off));
   }
   f32x16 dvt[C::DB], dkt[C::DB];
 #pragma unroll
   for (int cb = 0; cb < C::DB; ++cb) dvt[cb] = dkt[cb] = zero16();
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
+  DkdvTile<D> tile;
+  dkdv_load<D>(tile, rq, rdo, rlse, rdel, 0, tid);
+  dkdv_store<D>(tile, smem, 0, N, tid);
+  __syncthreads();
+
   for (int it = 0; it < nqt; ++it) {
-    const int q0 = it * C::BQ;
-    __syncthreads();   // previous tile fully consumed
-    for (int b = tid; b < 2 * C::NBLK; b += C::THREADS) {
-      const bool isq = b < C::NBLK;
-      const int bb = isq ? b : b - C::NBLK;
-      const int r0 = (bb / (D / 8)) * 4, col = (bb % (D / 8)) * 8;
-      u32x4 r[4];
-      load_block4x8<D>(r, (isq ? qh : doh), q0 + r0, col, N);
-      store_block4x8(r, isq ? Qs : dOs, C::P, isq ? Qt : dOt, r0, col);
-    }
-    if (tid < C::BQ) {
-      const int qi = q0 + tid;
-      lse2s[tid] = qi < N ? lseh[qi] * kLog2e : INFINITY;   // P = 0 past N
-      ds_[tid] = qi < N ? delh[qi] : 0.0f;
-    }
-    __syncthreads();
+    const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
+    const uint16_t* Qs = buf + C::OFF_QS;
+    const uint16_t* dOs = buf + C::OFF_DOS;
+    const uint16_t* Qt = buf + C::OFF_QT;
+    const uint16_t* dOt = buf + C::OFF_DOT;
+    const float* lse2s = reinterpret_cast<const float*>(buf + C::OFF_STATS);
+    const float* dls = lse2s + C::BQ;
+    const bool more = it + 1 < nqt;
+    if (more) dkdv_load<D>(tile, rq, rdo, rlse, rdel, (it + 1) * C::BQ, tid);
 
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -202,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int r = 0; r < 4; ++r) {
         const int qo = qb * 32 + 8 * r + 4 * g;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds_ + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qo);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p = fast_exp2(fmaf(s[qb][4 * r + e], c2, -l4[e]));
@@ -227,6 +267,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dkt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Qt + off)), sb, dkt[cb]);
       }
     }
+
+    if (more) dkdv_store<D>(tile, smem + ((it + 1) & 1) * C::BUF_ELEMS, (it + 1) * C::BQ, N, tid);
+    __syncthreads();
   }
 
   // dV^T / dK^T element i of block cb: column cb*32 + 8*(i/4) + 4g + i%4 of
@@ -257,21 +300,55 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 //   dP^T = V dO^T   (A = V rows from LDS, B = dO regs)
 //   P^T = 2^(c S^T - LSE log2 e), dS^T = P^T (dP^T - D)   (lane-uniform stats)
 //   dQ^T += K^T dS^T (A = K^T from LDS, B = dS^T from the accumulators)
+// Keys past N read as zero rows of K and V, so their dS multiplies a zero row
+// of K^T and adds nothing to dQ.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
   static constexpr int BQ = 128, BK = 64, THREADS = 256;
   static constexpr int P = D + 8;
   static constexpr int ROW_ELEMS = BK * P;
-  static constexpr int T_ELEMS = D * 64;  // transposed tile (tswz layout)
+  static constexpr int T_ELEMS = D * 64;     // transposed tile (tswz layout)
   static constexpr int OFF_KS = 0;
   static constexpr int OFF_VS = OFF_KS + ROW_ELEMS;
   static constexpr int OFF_KT = OFF_VS + ROW_ELEMS;
-  static constexpr int LDS_BYTES = (OFF_KT + T_ELEMS) * 2;
+  static constexpr int BUF_ELEMS = OFF_KT + T_ELEMS;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
   static constexpr int NBLK = (BK / 4) * (D / 8);
+  static constexpr int BLK_PER_T = 2 * NBLK / THREADS;   // K and V blocks per thread
   static constexpr int DK = D / 16, DB = D / 32;
   static_assert(BK == 64, "transposed tiles hold 64 positions per row");
+  static_assert((2 * NBLK) % THREADS == 0, "whole blocks per thread");
 };
+
+template <int D>
+struct DqTile {
+  u32x4 blk[DqCfg<D>::BLK_PER_T][4];
+};
+
+template <int D>
+__device__ __forceinline__ void dq_load(DqTile<D>& t, rsrc_t rk, rsrc_t rv, int k0, int tid) {
+  using C = DqCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::BLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    const bool isk = b < C::NBLK;
+    load_block<D>(t.blk[u], isk ? rk : rv, k0, isk ? b : b - C::NBLK);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_store(const DqTile<D>& t, uint16_t* buf, int tid) {
+  using C = DqCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::BLK_PER_T; ++u) {
+    const int b = tid + u * C::THREADS;
+    if (b < C::NBLK)
+      store_block<D>(t.blk[u], b, buf + C::OFF_KS, C::P, buf + C::OFF_KT);
+    else
+      store_block<D>(t.blk[u], b - C::NBLK, buf + C::OFF_VS, C::P, nullptr);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
@@ -281,15 +358,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     uint16_t* __restrict__ dq, int N, int nqt, float c2, float scale) {
   using C = DqCfg<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Ks = smem + C::OFF_KS;
-  uint16_t* Vs = smem + C::OFF_VS;
-  uint16_t* Kt = smem + C::OFF_KT;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
   const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* kh = k + hoff;
-  const uint16_t* vh = v + hoff;
+  const uint32_t hbytes = (uint32_t)N * D * 2;
+  const rsrc_t rk = make_rsrc(k + hoff, hbytes);
+  const rsrc_t rv = make_rsrc(v + hoff, hbytes);
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes);
+  const rsrc_t rdo = make_rsrc(dO + hoff, hbytes);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
@@ -298,13 +375,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   bf16x8 qreg[C::DK], oreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (qrow < N) {
-      a = *reinterpret_cast<const u32x4*>(q + hoff + (int64_t)qrow * D + kk * 16 + g * 8);
-      b = *reinterpret_cast<const u32x4*>(dO + hoff + (int64_t)qrow * D + kk * 16 + g * 8);
-    }
-    qreg[kk] = as_bf16x8(a);
-    oreg[kk] = as_bf16x8(b);
+    const uint32_t off = (uint32_t)((qrow * D + kk * 16 + g * 8) * 2);
+    qreg[kk] = as_bf16x8(buf_load16(rq, off));
+    oreg[kk] = as_bf16x8(buf_load16(rdo, off));
   }
   const float lse2 = qrow < N ? lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
   const float dl = qrow < N ? delta[(int64_t)bh * N + qrow] : 0.0f;
@@ -314,23 +387,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   for (int cb = 0; cb < C::DB; ++cb) dqt[cb] = zero16();
 
   const int nkt = (N + C::BK - 1) / C::BK;
+  DqTile<D> tile;
+  dq_load<D>(tile, rk, rv, 0, tid);
+  dq_store<D>(tile, smem, tid);
+  __syncthreads();
+
   for (int it = 0; it < nkt; ++it) {
-    const int k0 = it * C::BK;
-    __syncthreads();
-    for (int b = tid; b < 2 * C::NBLK; b += C::THREADS) {
-      const bool isk = b < C::NBLK;
-      const int bb = isk ? b : b - C::NBLK;
-      const int r0 = (bb / (D / 8)) * 4, col = (bb % (D / 8)) * 8;
-      u32x4 r[4];
-      load_block4x8<D>(r, isk ? kh : vh, k0 + r0, col, N);
-      if (isk) {
-        store_block4x8(r, Ks, C::P, Kt, r0, col);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(Vs + (r0 + i) * C::P + col) = r[i];
-      }
-    }
-    __syncthreads();
+    const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
+    const uint16_t* Ks = buf + C::OFF_KS;
+    const uint16_t* Vs = buf + C::OFF_VS;
+    const uint16_t* Kt = buf + C::OFF_KT;
+    const bool more = it + 1 < nkt;
+    if (more) dq_load<D>(tile, rk, rv, (it + 1) * C::BK, tid);
 
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -344,8 +412,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + off)), oreg[kk], dp[kb]);
       }
     }
-    // Keys past N are zero rows of K and V, so their dS multiplies a zero
-    // row of K^T below and adds nothing to dQ.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -366,6 +432,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         dqt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + off)), sb, dqt[cb]);
       }
     }
+
+    if (more) dq_store<D>(tile, smem + ((it + 1) & 1) * C::BUF_ELEMS, tid);
+    __syncthreads();
   }
 
   if (qrow < N) {

@@ -69,31 +69,26 @@ struct TileRegs {
   u32x4 v[FwdCfg<D>::VBLK_PER_T][4];
 };
 
-// Global -> registers for key tile starting at row r0 (rows >= N read as 0).
+// Global -> registers for key tile starting at row r0.  Buffer loads: rows
+// at or past N read as 0.
 template <int D>
-__device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, const uint16_t* __restrict__ kh,
-                                             const uint16_t* __restrict__ vh, int r0, int N,
+__device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, rsrc_t rk, rsrc_t rv, int r0,
                                              int tid) {
   using C = FwdCfg<D>;
 #pragma unroll
   for (int u = 0; u < C::KCH_PER_T; ++u) {
     const int cid = tid + u * C::THREADS;
     const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if ((C::KCH % C::THREADS == 0 || cid < C::KCH) && r0 + row < N)
-      val = *reinterpret_cast<const u32x4*>(kh + (int64_t)(r0 + row) * D + col);
-    t.k[u] = val;
+    t.k[u] = buf_load16(rk, (uint32_t)(((r0 + row) * D + col) * 2));
   }
 #pragma unroll
   for (int u = 0; u < C::VBLK_PER_T; ++u) {
     const int b = tid + u * C::THREADS;
     const int kq = b % (C::BC / 4), col = (b / (C::BC / 4)) * 8;
+    if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {   // wave-uniform
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if ((C::VBLK % C::THREADS == 0 || b < C::VBLK) && r0 + kq * 4 + r < N)
-        val = *reinterpret_cast<const u32x4*>(vh + (int64_t)(r0 + kq * 4 + r) * D + col);
-      t.v[u][r] = val;
+      for (int r = 0; r < 4; ++r)
+        t.v[u][r] = buf_load16(rv, (uint32_t)(((r0 + kq * 4 + r) * D + col) * 2));
     }
   }
 }
@@ -148,9 +143,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / ntq, qt = logical - bh * ntq;
   const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* qh = q + hoff;
-  const uint16_t* kh = k + hoff;
-  const uint16_t* vh = v + hoff;
+  const uint32_t hbytes = (uint32_t)N * D * 2;
+  const rsrc_t rq = make_rsrc(q + hoff, hbytes);
+  const rsrc_t rk = make_rsrc(k + hoff, hbytes);
+  const rsrc_t rv = make_rsrc(v + hoff, hbytes);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -162,9 +158,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   bf16x8 qreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (qrow < N) val = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + kk * 16 + g * 8);
-    qreg[kk] = as_bf16x8(val);
+    qreg[kk] = as_bf16x8(buf_load16(rq, (uint32_t)((qrow * D + kk * 16 + g * 8) * 2)));
   }
 
   f32x16 acc[C::DB];   // O^T blocks: rows = columns of O, col = this lane's query
@@ -175,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
   const int nkt = (N + C::BC - 1) / C::BC;
   TileRegs<D> tr;
-  load_kv_tile<D>(tr, kh, vh, 0, N, tid);
+  load_kv_tile<D>(tr, rk, rv, 0, tid);
   store_kv_tile<D>(tr, smem, smem + C::K_ELEMS, tid);
   __syncthreads();
 
@@ -183,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
     uint16_t* vt = ks + C::K_ELEMS;
     const bool more = j + 1 < nkt;
-    if (more) load_kv_tile<D>(tr, kh, vh, (j + 1) * C::BC, N, tid);
+    if (more) load_kv_tile<D>(tr, rk, rv, (j + 1) * C::BC, tid);
 
     // S^T = K_j Q^T: two 32-key blocks; A = K rows from LDS, B = Q^T.
     f32x16 s[2];

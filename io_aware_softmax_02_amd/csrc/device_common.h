@@ -62,6 +62,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resources: loads through them return 0 past `bytes`, which covers
+// the ragged last tile without branches.  The base must be wave-uniform;
+// byte offsets are 32-bit, so one resource spans at most 4 GiB (the API
+// limits one head of one tensor to 2 GiB).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit data format (CDNA)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_loadf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // max over the two lanes that share l % 32 (lanes l and l ^ 32).
 __device__ __forceinline__ float max_across_halves(float x) {
   return fmaxf(x, __shfl_xor(x, 32));

@@ -34,6 +34,9 @@ inline fa_status check_shape(const Shape& s, bool bf16) {
   if (s.empty()) return FA_OK;
   // Row indices inside the kernels are 32-bit.
   if (s.N > (int64_t(1) << 31) - 1) return FA_ERR_SHAPE;
+  // The bf16 kernels address one head of one tensor with 32-bit byte offsets
+  // (including a tile of rows past the end): at most 2 GiB per head.
+  if (bf16 && (s.N + 128) * s.d * 2 > (int64_t(1) << 31) - 1) return FA_ERR_SHAPE;
   // Overflow-safe product check.
   const int64_t lim = kMaxElems;
   if (s.B > lim || s.H > lim / s.B) return FA_ERR_SHAPE;
