@@ -26,6 +26,14 @@
 namespace fa {
 namespace {
 
+// LDS operands are read this many k-steps (S, dP) or (t, cb) steps (dV,
+// dK, dQ) ahead of the matrix-core instructions that use them; a scheduling
+// fence between the reads and the instructions keeps the compiler from
+// sinking each read next to its use, which would expose the LDS latency once
+// per instruction.
+constexpr int kReadAhead = 2;
+constexpr int kStepAhead = 4;
+
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   const int x = wg & 7, idx = wg >> 3;
   const int base = nwg >> 3, rem = nwg & 7;
@@ -223,16 +231,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bool more = it + 1 < nqt;
     if (more) dkdv_load<D>(tile, rq, rdo, rlse, rdel, (it + 1) * C::BQ, tid);
 
+    // S = Q K^T and dP = dO V^T for the two 32-query blocks: four
+    // independent accumulator chains, with the LDS operands of k-step kk+RA
+    // read before the instructions of step kk (see kReadAhead).
     f32x16 s[2], dp[2];
+    {
+      constexpr int RA = kReadAhead;
+      const uint16_t* qrow = Qs + li * C::P + g * 8;
+      const uint16_t* orow = dOs + li * C::P + g * 8;
+      bf16x8 qa[RA + 1][2], oa[RA + 1][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = zero16();
-      dp[qb] = zero16();
+      for (int kk = 0; kk < RA; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          qa[kk][qb] = lds_bf16x8(qrow + qb * 32 * C::P + kk * 16);
+          oa[kk][qb] = lds_bf16x8(orow + qb * 32 * C::P + kk * 16);
+        }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk) {
-        const int off = (qb * 32 + li) * C::P + kk * 16 + g * 8;
-        s[qb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Qs + off)), kreg[kk], s[qb]);
-        dp[qb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dOs + off)), vreg[kk], dp[qb]);
+        if (kk + RA < C::DK) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            qa[(kk + RA) % (RA + 1)][qb] = lds_bf16x8(qrow + qb * 32 * C::P + (kk + RA) * 16);
+            oa[(kk + RA) % (RA + 1)][qb] = lds_bf16x8(orow + qb * 32 * C::P + (kk + RA) * 16);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = mfma32(qa[kk % (RA + 1)][qb], kreg[kk], s[qb]);
+          dp[qb] = mfma32(oa[kk % (RA + 1)][qb], vreg[kk], dp[qb]);
+        }
       }
     }
     // P and dS; element i of block qb is query qb*32 + 8*(i/4) + 4g + i%4.
@@ -250,6 +281,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           dp[qb][4 * r + e] = p * (dp[qb][4 * r + e] - d4[e]);
         }
       }
+    // P and dS to bf16 B operands, one per 16-query step t.
+    bf16x8 pb[C::BQ / 16], sb[C::BQ / 16];
 #pragma unroll
     for (int t = 0; t < C::BQ / 16; ++t) {
       const int qb = t >> 1, h = t & 1;
@@ -259,12 +292,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         pw[e] = pack_bf16x2(s[qb][8 * h + 2 * e], s[qb][8 * h + 2 * e + 1]);
         sw[e] = pack_bf16x2(dp[qb][8 * h + 2 * e], dp[qb][8 * h + 2 * e + 1]);
       }
-      const bf16x8 pb = as_bf16x8(pw), sb = as_bf16x8(sw);
+      pb[t] = as_bf16x8(pw);
+      sb[t] = as_bf16x8(sw);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over steps n = (t, cb), operands
+    // read kStepAhead steps ahead.
+    {
+      constexpr int RA = kStepAhead, NS = (C::BQ / 16) * C::DB;
+      bf16x8 oa[RA + 1], qa[RA + 1];
 #pragma unroll
-      for (int cb = 0; cb < C::DB; ++cb) {
-        const int off = tswz(cb * 32 + li, t * 16 + g * 8);
-        dvt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(dOt + off)), pb, dvt[cb]);
-        dkt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Qt + off)), sb, dkt[cb]);
+      for (int n = 0; n < RA; ++n) {
+        const int off = tswz((n % C::DB) * 32 + li, (n / C::DB) * 16 + g * 8);
+        oa[n] = lds_bf16x8(dOt + off);
+        qa[n] = lds_bf16x8(Qt + off);
+      }
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        if (n + RA < NS) {
+          const int m = n + RA;
+          const int off = tswz((m % C::DB) * 32 + li, (m / C::DB) * 16 + g * 8);
+          oa[m % (RA + 1)] = lds_bf16x8(dOt + off);
+          qa[m % (RA + 1)] = lds_bf16x8(Qt + off);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = n / C::DB, cb = n % C::DB;
+        dvt[cb] = mfma32(oa[n % (RA + 1)], pb[t], dvt[cb]);
+        dkt[cb] = mfma32(qa[n % (RA + 1)], sb[t], dkt[cb]);
       }
     }
 
@@ -400,16 +453,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const bool more = it + 1 < nkt;
     if (more) dq_load<D>(tile, rk, rv, (it + 1) * C::BK, tid);
 
+    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks, operands
+    // read kReadAhead k-steps ahead.
     f32x16 s[2], dp[2];
+    {
+      constexpr int RA = kReadAhead;
+      const uint16_t* krow = Ks + li * C::P + g * 8;
+      const uint16_t* vrow = Vs + li * C::P + g * 8;
+      bf16x8 ka[RA + 1][2], va[RA + 1][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      dp[kb] = zero16();
+      for (int kk = 0; kk < RA; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          ka[kk][kb] = lds_bf16x8(krow + kb * 32 * C::P + kk * 16);
+          va[kk][kb] = lds_bf16x8(vrow + kb * 32 * C::P + kk * 16);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = zero16();
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk) {
-        const int off = (kb * 32 + li) * C::P + kk * 16 + g * 8;
-        s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + off)), qreg[kk], s[kb]);
-        dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + off)), oreg[kk], dp[kb]);
+        if (kk + RA < C::DK) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            ka[(kk + RA) % (RA + 1)][kb] = lds_bf16x8(krow + kb * 32 * C::P + (kk + RA) * 16);
+            va[(kk + RA) % (RA + 1)][kb] = lds_bf16x8(vrow + kb * 32 * C::P + (kk + RA) * 16);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma32(ka[kk % (RA + 1)][kb], qreg[kk], s[kb]);
+          dp[kb] = mfma32(va[kk % (RA + 1)][kb], oreg[kk], dp[kb]);
+        }
       }
     }
 #pragma unroll
@@ -419,17 +494,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         const float p = fast_exp2(fmaf(s[kb][i], c2, -lse2));
         dp[kb][i] = p * (dp[kb][i] - dl);
       }
+    bf16x8 sb[C::BK / 16];
 #pragma unroll
     for (int t = 0; t < C::BK / 16; ++t) {
       const int kb = t >> 1, h = t & 1;
       u32x4 sw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) sw[e] = pack_bf16x2(dp[kb][8 * h + 2 * e], dp[kb][8 * h + 2 * e + 1]);
-      const bf16x8 sb = as_bf16x8(sw);
+      sb[t] = as_bf16x8(sw);
+    }
+    // dQ^T += K^T dS^T over steps n = (t, cb), operands read kStepAhead
+    // steps ahead.
+    {
+      constexpr int RA = kStepAhead, NS = (C::BK / 16) * C::DB;
+      bf16x8 ka[RA + 1];
 #pragma unroll
-      for (int cb = 0; cb < C::DB; ++cb) {
-        const int off = tswz(cb * 32 + li, t * 16 + g * 8);
-        dqt[cb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + off)), sb, dqt[cb]);
+      for (int n = 0; n < RA; ++n)
+        ka[n] = lds_bf16x8(Kt + tswz((n % C::DB) * 32 + li, (n / C::DB) * 16 + g * 8));
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        if (n + RA < NS) {
+          const int m = n + RA;
+          ka[m % (RA + 1)] = lds_bf16x8(Kt + tswz((m % C::DB) * 32 + li, (m / C::DB) * 16 + g * 8));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int cb = n % C::DB;
+        dqt[cb] = mfma32(ka[n % (RA + 1)], sb[n / C::DB], dqt[cb]);
       }
     }
 

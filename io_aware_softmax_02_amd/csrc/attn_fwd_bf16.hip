@@ -12,10 +12,12 @@
 //   the only values written back (算珠楼的掌簿人, 技术解读).
 //
 // Work decomposition:
-//   workgroup = 128 query rows of one (batch, head); 4 waves x 32 rows.
-//   key tiles of 64 rows stream through LDS, double-buffered: the global
-//   loads of tile j+1 are issued before the math on tile j and written to
-//   the other LDS buffer after it, one barrier per tile.
+//   workgroup = 4 waves; each wave owns QB blocks of 32 query rows of one
+//   (batch, head).  Key tiles of BC rows stream through LDS, double-buffered:
+//   the buffer loads of tile j+1 are issued before the math on tile j and
+//   written to the other LDS buffer after it, one barrier per tile.  With
+//   QB = 2 every K and V operand read from LDS feeds two matrix-core
+//   instructions, halving LDS traffic per flop.
 //   Scores are formed transposed, S^T = K Q^T, so that each lane owns one
 //   query row: lane l holds query l%32 for 16 of every 32 keys (the other 16
 //   sit in lane l^32).  The row max and row sum are in-lane reductions plus
@@ -32,25 +34,29 @@ namespace {
 
 // Slack of the lazily updated softmax reference, in log2 units.
 constexpr float kSlack = 8.0f;
+// k-steps of K operands read from LDS ahead of their use.
+constexpr int kReadAhead = 2;
 
-template <int D>
+template <int D, int QB, int BC>
 struct FwdCfg {
-  static constexpr int BR = 128;           // query rows per workgroup
-  static constexpr int BC = 64;            // key rows per tile
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int KP = D + 8;         // K tile row pitch in LDS (bf16), +16 B pad
-  static constexpr int VP = BC + 8;        // V^T tile row pitch in LDS (bf16), +16 B pad
+  static constexpr int BR = WAVES * 32 * QB;      // query rows per workgroup
+  static constexpr int KB = BC / 32;              // 32-key blocks per tile
+  static constexpr int KP = D + 8;                // K tile row pitch in LDS (bf16), +16 B pad
+  static constexpr int VP = BC + 8;               // V^T tile row pitch in LDS (bf16), +16 B pad
   static constexpr int K_ELEMS = BC * KP;
   static constexpr int V_ELEMS = D * VP;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int KCH = BC * D / 8;               // 16-byte chunks of a K tile
+  static constexpr int KCH = BC * D / 8;                   // 16-byte chunks of a K tile
   static constexpr int KCH_PER_T = (KCH + THREADS - 1) / THREADS;
-  static constexpr int VBLK = (BC / 4) * (D / 8);       // 4-row x 8-col blocks of a V tile
+  static constexpr int VBLK = (BC / 4) * (D / 8);          // 4-row x 8-col blocks of a V tile
   static constexpr int VBLK_PER_T = (VBLK + THREADS - 1) / THREADS;
-  static constexpr int DK = D / 16;                     // k-steps of the QK^T contraction
-  static constexpr int DB = D / 32;                     // 32-column blocks of O
+  static constexpr int DK = D / 16;                        // k-steps of the QK^T contraction
+  static constexpr int DB = D / 32;                        // 32-column blocks of O
+  static_assert(BC % 32 == 0 && BC <= 128, "key tile is a multiple of 32 rows");
+  static_assert(KCH % THREADS == 0, "whole K chunks per thread");
 };
 
 // Maps the hardware workgroup id to a logical tile id so that consecutive
@@ -63,18 +69,19 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return x * base + (x < rem ? x : rem) + idx;
 }
 
-template <int D>
+template <class C>
 struct TileRegs {
-  u32x4 k[FwdCfg<D>::KCH_PER_T];
-  u32x4 v[FwdCfg<D>::VBLK_PER_T][4];
+  u32x4 k[C::KCH_PER_T];
+  u32x4 v[C::VBLK_PER_T][4];
 };
 
 // Global -> registers for key tile starting at row r0.  Buffer loads: rows
-// at or past N read as 0.
-template <int D>
-__device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, rsrc_t rk, rsrc_t rv, int r0,
+// at or past N read as 0.  V is read in 4-row x 8-column blocks, consecutive
+// lanes taking consecutive 4-row groups, so that the transposed LDS writes
+// of one instruction fill one contiguous row segment (no bank conflicts).
+template <int D, class C>
+__device__ __forceinline__ void load_kv_tile(TileRegs<C>& t, rsrc_t rk, rsrc_t rv, int r0,
                                              int tid) {
-  using C = FwdCfg<D>;
 #pragma unroll
   for (int u = 0; u < C::KCH_PER_T; ++u) {
     const int cid = tid + u * C::THREADS;
@@ -84,7 +91,7 @@ __device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, rsrc_t rk, rsrc_t r
 #pragma unroll
   for (int u = 0; u < C::VBLK_PER_T; ++u) {
     const int b = tid + u * C::THREADS;
-    const int kq = b % (C::BC / 4), col = (b / (C::BC / 4)) * 8;
+    const int kq = b % (C::VBLK / (D / 8)), col = (b / (C::VBLK / (D / 8))) * 8;
     if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {   // wave-uniform
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -95,23 +102,20 @@ __device__ __forceinline__ void load_kv_tile(TileRegs<D>& t, rsrc_t rk, rsrc_t r
 
 // Registers -> LDS: K row-major [BC][KP]; V transposed and key-permuted
 // [D][VP] (row c holds column c of V for the tile's keys).
-template <int D>
-__device__ __forceinline__ void store_kv_tile(const TileRegs<D>& t, uint16_t* ks, uint16_t* vt,
+template <int D, class C>
+__device__ __forceinline__ void store_kv_tile(const TileRegs<C>& t, uint16_t* ks, uint16_t* vt,
                                               int tid) {
-  using C = FwdCfg<D>;
 #pragma unroll
   for (int u = 0; u < C::KCH_PER_T; ++u) {
     const int cid = tid + u * C::THREADS;
-    if (C::KCH % C::THREADS == 0 || cid < C::KCH) {
-      const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(ks + row * C::KP + col) = t.k[u];
-    }
+    const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(ks + row * C::KP + col) = t.k[u];
   }
 #pragma unroll
   for (int u = 0; u < C::VBLK_PER_T; ++u) {
     const int b = tid + u * C::THREADS;
     if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {
-      const int kq = b % (C::BC / 4), col = (b / (C::BC / 4)) * 8;
+      const int kq = b % (C::VBLK / (D / 8)), col = (b / (C::VBLK / (D / 8))) * 8;
       const int key = kq * 4;                              // multiple of 4
       const int pos = (key & ~15) + kperm16(key & 15);     // 4 contiguous slots
 #pragma unroll
@@ -132,12 +136,12 @@ __device__ __forceinline__ void store_kv_tile(const TileRegs<D>& t, uint16_t* ks
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+template <int D, int QB, int BC, int MINW, bool PRIO>
+__global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int N,
     int ntq, float c2) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, QB, BC>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -151,149 +155,195 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
-  const int qrow = qt * C::BR + wave * 32 + li;   // this lane's query row
+  // query rows of this lane: qrow0 + 32*qb, qb = 0..QB-1
+  const int qrow0 = qt * C::BR + wave * 32 * QB + li;
 
   // Q^T as B operands, held for the whole loop: k-step kk covers columns
-  // kk*16 + 8g .. +7 of this lane's query row.
-  bf16x8 qreg[C::DK];
+  // kk*16 + 8g .. +7 of this lane's query rows.
+  bf16x8 qreg[QB][C::DK];
 #pragma unroll
-  for (int kk = 0; kk < C::DK; ++kk) {
-    qreg[kk] = as_bf16x8(buf_load16(rq, (uint32_t)((qrow * D + kk * 16 + g * 8) * 2)));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk)
+      qreg[qb][kk] = as_bf16x8(
+          buf_load16(rq, (uint32_t)(((qrow0 + 32 * qb) * D + kk * 16 + g * 8) * 2)));
+
+  f32x16 acc[QB][C::DB];   // O^T blocks: rows = columns of O, col = this lane's query
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[qb][db] = zero16();
+  float m_run[QB], l_run[QB];   // reference value (log2 units) and this lane's share of l
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
   }
 
-  f32x16 acc[C::DB];   // O^T blocks: rows = columns of O, col = this lane's query
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
-  float m_run = -INFINITY;   // running max of c*s, log2 units
-  float l_run = 0.0f;        // this lane's share of the running sum
-
-  const int nkt = (N + C::BC - 1) / C::BC;
-  TileRegs<D> tr;
-  load_kv_tile<D>(tr, rk, rv, 0, tid);
-  store_kv_tile<D>(tr, smem, smem + C::K_ELEMS, tid);
+  const int nkt = (N + BC - 1) / BC;
+  TileRegs<C> tr;
+  load_kv_tile<D, C>(tr, rk, rv, 0, tid);
+  store_kv_tile<D, C>(tr, smem, smem + C::K_ELEMS, tid);
   __syncthreads();
 
   for (int j = 0; j < nkt; ++j) {
-    uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
-    uint16_t* vt = ks + C::K_ELEMS;
+    const uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
+    const uint16_t* vt = ks + C::K_ELEMS;
     const bool more = j + 1 < nkt;
-    if (more) load_kv_tile<D>(tr, rk, rv, (j + 1) * C::BC, tid);
 
-    // S^T = K_j Q^T: two 32-key blocks; A = K rows from LDS, B = Q^T.
-    f32x16 s[2];
+    // S^T = K_j Q^T in 32-key blocks; A = K rows from LDS (each read feeds
+    // the QB query blocks), B = Q^T.  The K operands are read kReadAhead
+    // k-steps ahead of the instructions that use them (a scheduling fence
+    // keeps the compiler from sinking the reads next to their uses, which
+    // would expose the LDS latency once per instruction), and the key blocks
+    // alternate so that consecutive matrix-core instructions are independent.
+    constexpr int RA = kReadAhead;
+    f32x16 s[QB][C::KB];
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+    const uint16_t* krow = ks + li * C::KP + g * 8;
+    bf16x8 kop[RA + 1][C::KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
+    for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(ks + (kb * 32 + li) * C::KP + kk * 16 + g * 8));
-        s[kb] = mfma32(a, qreg[kk], s[kb]);
+      for (int kb = 0; kb < C::KB; ++kb)
+        kop[kk][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + kb * 32 * C::KP + kk * 16));
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) {
+      if (kk + RA < C::DK) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+          kop[(kk + RA) % (RA + 1)][kb] = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(krow + kb * 32 * C::KP + (kk + RA) * 16));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = mfma32(kop[kk % (RA + 1)][kb], qreg[qb][kk], s[qb][kb]);
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
+    // The next tile's loads go out now, to overlap the softmax and O += P V.
+    if (more) load_kv_tile<D, C>(tr, rk, rv, (j + 1) * BC, tid);
     // Keys past N in the last tile do not exist: their scores are -inf.
-    if (j * C::BC + C::BC > N) {
+    if (j * BC + BC > N) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * C::BC + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= N) s[kb][i] = -INFINITY;
-        }
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j * BC + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= N) s[qb][kb][i] = -INFINITY;
+          }
     }
-    // Online softmax for this lane's query row.  The reference value m_run
-    // moves only when some row of the wave sees a score more than 2^kSlack
-    // above it; until then the factor 2^(m_old - m_new) would be 1 for the
-    // rows that did not grow and the rescale is skipped.  P~ = 2^(c s - m_run)
-    // then stays <= 2^kSlack, and because U and l share the same reference
-    // value the result O = U / l is unchanged (the rescale identity holds for
-    // any common reference, not only the running maximum).
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_across_halves(mx);
-    const float m_cand = mx * c2;
-    if (__any(m_cand > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, m_cand);
-      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_run = m_new;
-    }
-    // P~ in fp32 for the row sum, rounded to bf16 (RNE) in the B-operand
-    // layout of the next contraction.
-    bf16x8 pb[C::BC / 16];
-    float rs = 0.0f;
-#pragma unroll
-    for (int t = 0; t < C::BC / 16; ++t) {
-      const int kb = t >> 1, h = t & 1;
-      u32x4 pw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(s[kb][8 * h + 2 * e], c2, -m_run));
-        const float p1 = fast_exp2(fmaf(s[kb][8 * h + 2 * e + 1], c2, -m_run));
-        rs += p0 + p1;
-        pw[e] = pack_bf16x2(p0, p1);
-      }
-      pb[t] = as_bf16x8(pw);
-    }
-    l_run += rs;
 
-    // O^T += V_j^T P^T in 16-key steps (elements 8h..8h+7 of score block kb
-    // hold the step's keys in the operand's k order).
+    // Online softmax for each of this lane's query rows.  The reference
+    // value m_run moves only when some row of the wave sees a score more
+    // than 2^kSlack above it; until then the factor 2^(m_old - m_new) would
+    // be 1 for the rows that did not grow and the rescale is skipped.
+    // P~ = 2^(c s - m_run) then stays <= 2^kSlack, and because U and l share
+    // the same reference value the result O = U / l is unchanged (the
+    // rescale identity holds for any common reference, not only the maximum).
+    bf16x8 pb[QB][BC / 16];
 #pragma unroll
-    for (int t = 0; t < C::BC / 16; ++t) {
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+      mx = max_across_halves(mx);
+      const float m_cand = mx * c2;
+      if (__any(m_cand > m_run[qb] + kSlack)) {
+        const float m_new = fmaxf(m_run[qb], m_cand);
+        const float alpha = fast_exp2(m_run[qb] - m_new);   // 0 on the first tile
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
+        m_run[qb] = m_new;
+      }
+      // P~ in fp32 for the row sum, rounded to bf16 (RNE) in the B-operand
+      // layout of the next contraction: elements 8h..8h+7 of score block kb
+      // hold the keys of 16-key step t = 2 kb + h in the operand's k order.
+      float rs = 0.0f;
+#pragma unroll
+      for (int t = 0; t < BC / 16; ++t) {
+        const int kb = t >> 1, h = t & 1;
+        u32x4 pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e], c2, -m_run[qb]));
+          const float p1 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e + 1], c2, -m_run[qb]));
+          rs += p0 + p1;
+          pw[e] = pack_bf16x2(p0, p1);
+        }
+        pb[qb][t] = as_bf16x8(pw);
+      }
+      l_run[qb] += rs;
+    }
+
+    // O^T += V_j^T P^T in 16-key steps; each V^T read feeds the QB blocks.
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int t = 0; t < BC / 16; ++t) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
         const bf16x8 a = as_bf16x8(
             *reinterpret_cast<const u32x4*>(vt + (db * 32 + li) * C::VP + t * 16 + g * 8));
-        acc[db] = mfma32(a, pb[t], acc[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][t], acc[qb][db]);
       }
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
 
-    if (more) store_kv_tile<D>(tr, smem + ((j + 1) & 1) * C::BUF_ELEMS,
-                               smem + ((j + 1) & 1) * C::BUF_ELEMS + C::K_ELEMS, tid);
+    if (more) {
+      uint16_t* nb = smem + ((j + 1) & 1) * C::BUF_ELEMS;
+      store_kv_tile<D, C>(tr, nb, nb + C::K_ELEMS, tid);
+    }
     __syncthreads();
   }
 
   // Epilogue: O = U / l, LSE = ln2 * (m + log2 l).
-  const float l_tot = sum_across_halves(l_run);
-  if (qrow < N) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = o + hoff + (int64_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qrow0 + 32 * qb;
+    const float l_tot = sum_across_halves(l_run[qb]);
+    if (qrow < N) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = o + hoff + (int64_t)qrow * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * r + 0] * inv, acc[db][4 * r + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * g) = w;
-      }
-    if (g == 0) lse[(int64_t)bh * N + qrow] = kLn2 * (m_run + log2f(l_tot));
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[qb][db][4 * r + 0] * inv, acc[qb][db][4 * r + 1] * inv);
+          w[1] = pack_bf16x2(acc[qb][db][4 * r + 2] * inv, acc[qb][db][4 * r + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * g) = w;
+        }
+      if (g == 0) lse[(int64_t)bh * N + qrow] = kLn2 * (m_run[qb] + log2f(l_tot));
+    }
   }
 }
 
-template <int D>
+template <int D, int QB, int BC, int MINW, bool PRIO>
 int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
            int64_t BH, int64_t N, float scale, hipStream_t stream) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, QB, BC>;
   const int ntq = (int)((N + C::BR - 1) / C::BR);
   const int64_t nwg = (int64_t)ntq * BH;
-  static bool attr_set = false;  // idempotent; a race only repeats the call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return (int)e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)nwg), dim3(C::THREADS), C::LDS_BYTES,
-                     stream, q, k, v, o, lse, (int)N, ntq, scale * kLog2e);
+  auto kern = fwd_bf16_kernel<D, QB, BC, MINW, PRIO>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(C::THREADS), C::LDS_BYTES, stream, q, k,
+                     v, o, lse, (int)N, ntq, scale * kLog2e);
   return (int)hipGetLastError();
 }
 
@@ -305,8 +355,8 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   const auto* k16 = static_cast<const uint16_t*>(k);
   const auto* v16 = static_cast<const uint16_t*>(v);
   auto* o16 = static_cast<uint16_t*>(o);
-  if (d == 128) return launch<128>(q16, k16, v16, o16, lse, BH, N, scale, stream);
-  return launch<64>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+  if (d == 128) return launch<128, 1, 64, 2, false>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+  return launch<64, 1, 64, 2, false>(q16, k16, v16, o16, lse, BH, N, scale, stream);
 }
 
 }  // namespace fa

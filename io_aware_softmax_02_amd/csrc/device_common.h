@@ -60,6 +60,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 16-byte LDS read of 8 bf16 (address 16-byte aligned).
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Buffer resources: loads through them return 0 past `bytes`, which covers
@@ -80,13 +85,19 @@ __device__ __forceinline__ float buf_loadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// max over the two lanes that share l % 32 (lanes l and l ^ 32).
+// Lanes l and l ^ 32 exchange a value with v_permlane32_swap: called with
+// the same register twice, the two results hold x[l % 32] and x[l % 32 + 32]
+// in every lane (a VALU op, no LDS round trip).
 __device__ __forceinline__ float max_across_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_across_halves(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Position of key k (0..15) inside a 16-key group of a "k-permuted" LDS row.
