@@ -14,28 +14,30 @@
 // Work decomposition:
 //   workgroup = 4 waves; each wave owns QB blocks of 32 query rows of one
 //   (batch, head).  Key tiles of BC rows stream through LDS, double-buffered:
-//   the buffer loads of tile j+1 are issued before the math on tile j and
-//   written to the other LDS buffer after it, one barrier per tile.  With
-//   QB = 2 every K and V operand read from LDS feeds two matrix-core
-//   instructions, halving LDS traffic per flop.
+//   direct buffer->LDS loads of tile j+1 are issued at the start of tile j
+//   (no registers involved), one barrier per tile.  With QB = 2 every K and V
+//   operand read from LDS feeds two matrix-core instructions, halving LDS
+//   traffic per flop.
 //   Scores are formed transposed, S^T = K Q^T, so that each lane owns one
 //   query row: lane l holds query l%32 for 16 of every 32 keys (the other 16
 //   sit in lane l^32).  The row max and row sum are in-lane reductions plus
 //   one exchange between the two half-waves.  The probabilities leave the
 //   score accumulators already in the B-operand layout of O^T += V^T P^T, so
-//   P never touches LDS; V is written to LDS transposed, with the keys of
-//   each 16-key step permuted to match (see kperm16).
+//   P never touches LDS; the V^T operand is gathered from the row-major V
+//   tile with transposing LDS reads in the matching key order (lds_tile.h).
 //   Base-2 domain: c = scale * log2(e); p = 2^(c s - m) with m in log2 units;
 //   LSE = ln 2 * (m + log2 l).
-#include "device_common.h"
+#include "lds_tile.h"
 
 namespace fa {
 namespace {
 
 // Slack of the lazily updated softmax reference, in log2 units.
 constexpr float kSlack = 8.0f;
-// k-steps of K operands read from LDS ahead of their use.
+// k-steps of K operands, and (t, db) steps of V^T operands, read from LDS
+// ahead of their use.
 constexpr int kReadAhead = 2;
+constexpr int kStepAhead = 4;
 
 template <int D, int QB, int BC>
 struct FwdCfg {
@@ -43,20 +45,12 @@ struct FwdCfg {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = WAVES * 32 * QB;      // query rows per workgroup
   static constexpr int KB = BC / 32;              // 32-key blocks per tile
-  static constexpr int KP = D + 8;                // K tile row pitch in LDS (bf16), +16 B pad
-  static constexpr int VP = BC + 8;               // V^T tile row pitch in LDS (bf16), +16 B pad
-  static constexpr int K_ELEMS = BC * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int TILE = BC * D;             // one K or V tile (bf16), swizzled
+  static constexpr int BUF_ELEMS = 2 * TILE;      // K tile then V tile
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int KCH = BC * D / 8;                   // 16-byte chunks of a K tile
-  static constexpr int KCH_PER_T = (KCH + THREADS - 1) / THREADS;
-  static constexpr int VBLK = (BC / 4) * (D / 8);          // 4-row x 8-col blocks of a V tile
-  static constexpr int VBLK_PER_T = (VBLK + THREADS - 1) / THREADS;
-  static constexpr int DK = D / 16;                        // k-steps of the QK^T contraction
-  static constexpr int DB = D / 32;                        // 32-column blocks of O
+  static constexpr int DK = D / 16;               // k-steps of the QK^T contraction
+  static constexpr int DB = D / 32;               // 32-column blocks of O
   static_assert(BC % 32 == 0 && BC <= 128, "key tile is a multiple of 32 rows");
-  static_assert(KCH % THREADS == 0, "whole K chunks per thread");
 };
 
 // Maps the hardware workgroup id to a logical tile id so that consecutive
@@ -67,73 +61,6 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   const int x = wg & 7, idx = wg >> 3;
   const int base = nwg >> 3, rem = nwg & 7;
   return x * base + (x < rem ? x : rem) + idx;
-}
-
-template <class C>
-struct TileRegs {
-  u32x4 k[C::KCH_PER_T];
-  u32x4 v[C::VBLK_PER_T][4];
-};
-
-// Global -> registers for key tile starting at row r0.  Buffer loads: rows
-// at or past N read as 0.  V is read in 4-row x 8-column blocks, consecutive
-// lanes taking consecutive 4-row groups, so that the transposed LDS writes
-// of one instruction fill one contiguous row segment (no bank conflicts).
-template <int D, class C>
-__device__ __forceinline__ void load_kv_tile(TileRegs<C>& t, rsrc_t rk, rsrc_t rv, int r0,
-                                             int tid) {
-#pragma unroll
-  for (int u = 0; u < C::KCH_PER_T; ++u) {
-    const int cid = tid + u * C::THREADS;
-    const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
-    t.k[u] = buf_load16(rk, (uint32_t)(((r0 + row) * D + col) * 2));
-  }
-#pragma unroll
-  for (int u = 0; u < C::VBLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    const int kq = b % (C::VBLK / (D / 8)), col = (b / (C::VBLK / (D / 8))) * 8;
-    if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {   // wave-uniform
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        t.v[u][r] = buf_load16(rv, (uint32_t)(((r0 + kq * 4 + r) * D + col) * 2));
-    }
-  }
-}
-
-// Registers -> LDS: K row-major [BC][KP]; V transposed and key-permuted
-// [D][VP] (row c holds column c of V for the tile's keys).
-template <int D, class C>
-__device__ __forceinline__ void store_kv_tile(const TileRegs<C>& t, uint16_t* ks, uint16_t* vt,
-                                              int tid) {
-#pragma unroll
-  for (int u = 0; u < C::KCH_PER_T; ++u) {
-    const int cid = tid + u * C::THREADS;
-    const int row = cid / (D / 8), col = (cid % (D / 8)) * 8;
-    *reinterpret_cast<u32x4*>(ks + row * C::KP + col) = t.k[u];
-  }
-#pragma unroll
-  for (int u = 0; u < C::VBLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    if (C::VBLK % C::THREADS == 0 || b < C::VBLK) {
-      const int kq = b % (C::VBLK / (D / 8)), col = (b / (C::VBLK / (D / 8))) * 8;
-      const int key = kq * 4;                              // multiple of 4
-      const int pos = (key & ~15) + kperm16(key & 15);     // 4 contiguous slots
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int w = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = (t.v[u][0][w] >> 16) | (t.v[u][1][w] & 0xffff0000u);
-          hi = (t.v[u][2][w] >> 16) | (t.v[u][3][w] & 0xffff0000u);
-        } else {
-          lo = (t.v[u][0][w] & 0xffffu) | (t.v[u][1][w] << 16);
-          hi = (t.v[u][2][w] & 0xffffu) | (t.v[u][3][w] << 16);
-        }
-        u32x2 pr = {lo, hi};
-        *reinterpret_cast<u32x2*>(vt + (col + c) * C::VP + pos) = pr;
-      }
-    }
-  }
 }
 
 template <int D, int QB, int BC, int MINW, bool PRIO>
@@ -153,7 +80,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
   const rsrc_t rv = make_rsrc(v + hoff, hbytes);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, g = lane >> 5;
   // query rows of this lane: qrow0 + 32*qb, qb = 0..QB-1
   const int qrow0 = qt * C::BR + wave * 32 * QB + li;
@@ -181,15 +108,19 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
   }
 
   const int nkt = (N + BC - 1) / BC;
-  TileRegs<C> tr;
-  load_kv_tile<D, C>(tr, rk, rv, 0, tid);
-  store_kv_tile<D, C>(tr, smem, smem + C::K_ELEMS, tid);
+  tile_load<D, BC, C::WAVES>(smem, rk, 0, wave, lane);
+  tile_load<D, BC, C::WAVES>(smem + C::TILE, rv, 0, wave, lane);
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < nkt; ++j) {
     const uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
-    const uint16_t* vt = ks + C::K_ELEMS;
-    const bool more = j + 1 < nkt;
+    const uint16_t* vs = ks + C::TILE;
+    if (j + 1 < nkt) {
+      uint16_t* nb = smem + ((j + 1) & 1) * C::BUF_ELEMS;
+      tile_load<D, BC, C::WAVES>(nb, rk, (j + 1) * BC, wave, lane);
+      tile_load<D, BC, C::WAVES>(nb + C::TILE, rv, (j + 1) * BC, wave, lane);
+    }
 
     // S^T = K_j Q^T in 32-key blocks; A = K rows from LDS (each read feeds
     // the QB query blocks), B = Q^T.  The K operands are read kReadAhead
@@ -200,13 +131,11 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
     constexpr int RA = kReadAhead;
     f32x16 s[QB][C::KB];
     if (PRIO) __builtin_amdgcn_s_setprio(1);
-    const uint16_t* krow = ks + li * C::KP + g * 8;
     bf16x8 kop[RA + 1][C::KB];
 #pragma unroll
     for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-        kop[kk][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + kb * 32 * C::KP + kk * 16));
+      for (int kb = 0; kb < C::KB; ++kb) kop[kk][kb] = row_operand<D>(ks, kb * 32 + li, 2 * kk + g);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -216,8 +145,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
       if (kk + RA < C::DK) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
-          kop[(kk + RA) % (RA + 1)][kb] = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(krow + kb * 32 * C::KP + (kk + RA) * 16));
+          kop[(kk + RA) % (RA + 1)][kb] = row_operand<D>(ks, kb * 32 + li, 2 * (kk + RA) + g);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -227,8 +155,6 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
           s[qb][kb] = mfma32(kop[kk % (RA + 1)][kb], qreg[qb][kk], s[qb][kb]);
     }
     if (PRIO) __builtin_amdgcn_s_setprio(0);
-    // The next tile's loads go out now, to overlap the softmax and O += P V.
-    if (more) load_kv_tile<D, C>(tr, rk, rv, (j + 1) * BC, tid);
     // Keys past N in the last tile do not exist: their scores are -inf.
     if (j * BC + BC > N) {
 #pragma unroll
@@ -289,25 +215,32 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
       l_run[qb] += rs;
     }
 
-    // O^T += V_j^T P^T in 16-key steps; each V^T read feeds the QB blocks.
+    // O^T += V_j^T P^T over steps n = (t, db): 16-key step t, 32-column
+    // block db.  The V^T operand of a step is gathered with transposing
+    // reads kStepAhead steps ahead (behind a scheduling fence) and feeds the
+    // QB query blocks.
     if (PRIO) __builtin_amdgcn_s_setprio(1);
+    {
+      constexpr int SA = kStepAhead, NS = (BC / 16) * C::DB;
+      bf16x8 vop[SA + 1];
 #pragma unroll
-    for (int t = 0; t < BC / 16; ++t) {
+      for (int n = 0; n < SA; ++n) vop[n] = tr_operand<D>(vs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(vt + (db * 32 + li) * C::VP + t * 16 + g * 8));
+      for (int n = 0; n < NS; ++n) {
+        if (n + SA < NS) {
+          const int m = n + SA;
+          vop[m % (SA + 1)] = tr_operand<D>(vs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = n / C::DB, db = n % C::DB;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][t], acc[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(vop[n % (SA + 1)], pb[qb][t], acc[qb][db]);
       }
     }
     if (PRIO) __builtin_amdgcn_s_setprio(0);
 
-    if (more) {
-      uint16_t* nb = smem + ((j + 1) & 1) * C::BUF_ELEMS;
-      store_kv_tile<D, C>(tr, nb, nb + C::K_ELEMS, tid);
-    }
-    __syncthreads();
+    wait_vmem();      // this wave's loads of tile j+1 have landed in LDS
+    __syncthreads();  // ... and everyone's; tile j is no longer read
   }
 
   // Epilogue: O = U / l, LSE = ln2 * (m + log2 l).

@@ -81,6 +81,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Waits until every vector-memory load this wave issued has completed,
+// including direct buffer->LDS loads.
+// (s_waitcnt vmcnt(0): vmcnt bits 0 in [3:0] and [15:14], expcnt 7 in [6:4],
+// lgkmcnt 15 in [11:8].  The builtin, unlike inline assembly, is seen by the
+// compiler's own wait insertion.)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float buf_loadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

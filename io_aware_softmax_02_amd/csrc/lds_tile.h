@@ -1,0 +1,114 @@
+// Row-major bf16 tiles in LDS, filled by direct buffer->LDS loads and read
+// either along rows (16-byte reads) or across rows (transposing reads).
+//
+// Layout.  A tile holds rows of D bf16 values (2*D bytes, no padding).  Each
+// row is a sequence of 16-byte chunks; logical chunk c of row r is stored at
+// physical chunk c ^ swz(r), swz(r) = 2*(r & 3) + ((r >> 2) & 1) (a 3-bit
+// XOR, so a chunk never leaves its group of eight).  Two read patterns are
+// then free of LDS bank conflicts:
+//   - 8 consecutive rows, same logical chunk (matrix-core operand rows):
+//     swz takes 8 distinct values on any 8 consecutive rows;
+//   - 4 consecutive rows starting at a multiple of 4, two adjacent chunks
+//     (the transposing reads): swz takes the values {0,2,4,6} + b there, so
+//     the four chunk pairs land on four distinct pairs.
+//
+// Loads.  A direct buffer->LDS load writes lane L's 16 bytes at LDS address
+// M0 + 16 L whatever global address the lane read, so the swizzle is applied
+// on the global side: the lane that fills physical chunk p of row r reads
+// logical chunk p ^ swz(r) of that row.  Reads past the end of the buffer
+// resource return zeros.
+//
+// Transposing read.  ds_read_b64_tr_b16 works on groups of 16 lanes: source
+// lane 4a + b supplies the address of 4 consecutive bf16 values, and result
+// lane i receives element i % 4 of source lanes i/4, i/4 + 4, i/4 + 8 and
+// i/4 + 12.  tr_operand uses it twice to give lane l (column cbase + l % 32,
+// k-group g = l / 32) the values of rows rb + kperm-order keys
+// {4g..4g+3, 8+4g..8+4g+3} of that column: exactly the operand a 32x32x16
+// matrix-core instruction needs when its contraction index runs along the
+// tile's rows and the other operand comes from score accumulators.
+#pragma once
+
+#include "device_common.h"
+
+namespace fa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// Offset (bf16 elements) of logical chunk c of row r in a tile with D columns.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * D + ((c ^ swz(r)) << 3);
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct buffer->LDS load of 16 bytes per lane: lane L's bytes land at
+// LDS byte address lds + 16 L (lds wave-uniform).  Issued as inline assembly
+// so that the compiler does not order later LDS reads of *other* buffers
+// behind it; completion is awaited explicitly (wait_vmem) before the barrier
+// that publishes the tile.  M0 is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
+}
+
+// Copies rows [r0, r0 + R) of one head of a [N][D] bf16 matrix into a tile.
+// The R*D/8 chunks go out as 64-chunk wave instructions; wave w of NW issues
+// instructions w, w + NW, ...  Rows at or past the end of `src` read as 0.
+// `wave` must be wave-uniform (an SGPR value).
+template <int D, int R, int NW>
+__device__ __forceinline__ void tile_load(uint16_t* tile, rsrc_t src, int r0, int wave, int lane) {
+  constexpr int NC = D / 8;               // chunks per row
+  constexpr int NI = R * NC / 64;          // wave instructions per tile
+  static_assert((R * NC) % 64 == 0, "whole wave instructions per tile");
+  static_assert(NI % NW == 0, "the same number of instructions for every wave");
+#pragma unroll
+  for (int u = 0; u < NI / NW; ++u) {
+    const int i = wave + u * NW;
+    const int lin = i * 64 + lane;         // physical chunk position in the tile
+    const int row = lin / NC, phys = lin % NC;
+    const int c = phys ^ swz(row);
+    const uint32_t off = (uint32_t)(((r0 + row) * D + c * 8) * 2);
+    lds_dma16(src, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + i * 64 * 8)));
+  }
+}
+
+// Row operand: 8 values of logical chunk c of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r, int c) {
+  return lds_bf16x8(tile + tile_off<D>(r, c));
+}
+
+// Transposed operand: for lane l, column cbase + l % 32 of rows
+// rb + {4g, 4g+1, 4g+2, 4g+3, 8+4g, ..., 8+4g+3} (g = l / 32), in that order.
+// rb must be a multiple of 16 and cbase a multiple of 32.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int rb, int cbase, int lane) {
+  const int i16 = lane & 15, q = lane >> 4;
+  const int a = i16 >> 2, b = i16 & 3, g = q >> 1;
+  const int col = cbase + 16 * (q & 1) + 4 * b;     // 4 consecutive columns
+  const int r1 = rb + 4 * g + a, r2 = r1 + 8;
+  const uint16_t* p1 = tile + tile_off<D>(r1, col >> 3) + (col & 7);
+  const uint16_t* p2 = tile + tile_off<D>(r2, col >> 3) + (col & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p1));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p2));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
+  return as_bf16x8(w);
+}
+
+}  // namespace fa
