@@ -11,17 +11,17 @@
 // every output is written once, in a fixed order, without atomics.
 //
 // Matrix-core layout as in device_common.h.  Each contraction keeps one
-// operand in registers and reads the other from LDS; an operand whose
-// contraction index runs along a tile's rows (Q^T in dK, dO^T in dV, K^T in
-// dQ) is stored transposed and key/query-permuted (kperm16, tswz) so that
-// the 8 values a lane needs are one 16-byte read and line up with the score
-// accumulator layout that supplies the other operand.
+// operand in registers and reads the other from a row-major LDS tile
+// (lds_tile.h): along rows for S, dP and their transposes, and with
+// transposing reads for the operands whose contraction index runs along the
+// tile's rows (Q^T in dK, dO^T in dV, K^T in dQ), in the key/query order of
+// the score accumulators that supply the other operand.
 //
-// Streaming: the tiles of the loop are fetched with buffer loads (reads past
-// the end of a head return 0, which is what a ragged last tile needs) into
-// registers one tile ahead, and written to the other half of a double-buffered
-// LDS area after the math on the current tile; one barrier per tile.
-#include "device_common.h"
+// Streaming: the tiles of the loop are fetched one tile ahead with direct
+// buffer->LDS loads (reads past the end of a head return 0, which is what a
+// ragged last tile needs) into the other half of a double-buffered LDS
+// area; one barrier per tile.
+#include "lds_tile.h"
 
 namespace fa {
 namespace {
@@ -67,45 +67,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (row < rows && tid % LPR == 0) delta[row] = s;
 }
 
-// A tile of 64 rows x D columns is handled as 4-row x 8-column blocks; block
-// b covers rows 4*(b / (D/8)) .. +3 and columns 8*(b % (D/8)) .. +7 (consecutive
-// lanes along a row, so the row-major LDS writes are conflict-free).
-template <int D>
-__device__ __forceinline__ void load_block(u32x4 (&r)[4], rsrc_t src, int row0, int b) {
-  const int r0 = (b / (D / 8)) * 4, col = (b % (D / 8)) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = buf_load16(src, (uint32_t)(((row0 + r0 + i) * D + col) * 2));
-}
-
-// Writes a loaded block row-major into an LDS tile with pitch P (if given) and
-// transposed + permuted into a swizzled 64-position tile (if given).
-template <int D>
-__device__ __forceinline__ void store_block(const u32x4 (&r)[4], int b, uint16_t* rowmajor, int P,
-                                            uint16_t* trans) {
-  const int r0 = (b / (D / 8)) * 4, col = (b % (D / 8)) * 8;
-  if (rowmajor) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rowmajor + (r0 + i) * P + col) = r[i];
-  }
-  if (trans) {
-    const int pos = (r0 & ~15) + kperm16(r0 & 15);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = c >> 1;
-      uint32_t lo, hi;
-      if (c & 1) {
-        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-      } else {
-        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-      }
-      u32x2 pr = {lo, hi};
-      *reinterpret_cast<u32x2*>(trans + tswz(col + c, pos)) = pr;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // dK / dV: workgroup owns 128 keys (4 waves x 32), loops over 64-query tiles.
 // Per wave and tile (lane l: key l%32 of the wave's block, k-group g):
@@ -117,65 +78,16 @@ __device__ __forceinline__ void store_block(const u32x4 (&r)[4], int b, uint16_t
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
-  static constexpr int BK = 128, BQ = 64, THREADS = 256;
-  static constexpr int P = D + 8;            // row-major tile pitch (bf16)
-  static constexpr int ROW_ELEMS = BQ * P;
-  static constexpr int T_ELEMS = D * 64;     // transposed tiles (tswz layout)
-  // One buffer: Qs, dOs (row-major), Qt, dOt (transposed), lse2[BQ], delta[BQ]
-  static constexpr int OFF_QS = 0;
-  static constexpr int OFF_DOS = OFF_QS + ROW_ELEMS;
-  static constexpr int OFF_QT = OFF_DOS + ROW_ELEMS;
-  static constexpr int OFF_DOT = OFF_QT + T_ELEMS;
-  static constexpr int OFF_STATS = OFF_DOT + T_ELEMS;   // bf16 units; 2*BQ floats follow
+  static constexpr int BK = 128, BQ = 64, WAVES = 4, THREADS = 64 * WAVES;
+  static constexpr int TILE = BQ * D;          // one Q or dO tile (bf16), swizzled
+  // One buffer: Q tile, dO tile, lse2[BQ], delta[BQ]
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_DO = TILE;
+  static constexpr int OFF_STATS = 2 * TILE;   // bf16 units; 2*BQ floats follow
   static constexpr int BUF_ELEMS = OFF_STATS + 4 * BQ;
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int NBLK = (BQ / 4) * (D / 8);         // blocks per matrix per tile
-  static constexpr int BLK_PER_T = 2 * NBLK / THREADS;   // Q and dO blocks per thread
   static constexpr int DK = D / 16, DB = D / 32;
-  static_assert(BQ == 64, "transposed tiles hold 64 positions per row");
-  static_assert((2 * NBLK) % THREADS == 0, "whole blocks per thread");
 };
-
-template <int D>
-struct DkdvTile {
-  u32x4 blk[DkdvCfg<D>::BLK_PER_T][4];
-  float stat;
-};
-
-template <int D>
-__device__ __forceinline__ void dkdv_load(DkdvTile<D>& t, rsrc_t rq, rsrc_t rdo, rsrc_t rlse,
-                                          rsrc_t rdel, int q0, int tid) {
-  using C = DkdvCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::BLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    const bool isq = b < C::NBLK;
-    load_block<D>(t.blk[u], isq ? rq : rdo, q0, isq ? b : b - C::NBLK);
-  }
-  t.stat = 0.0f;
-  if (tid < 2 * C::BQ) t.stat = buf_loadf(tid < C::BQ ? rlse : rdel,
-                                         (uint32_t)((q0 + (tid & (C::BQ - 1))) * 4));
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_store(const DkdvTile<D>& t, uint16_t* buf, int q0, int N,
-                                           int tid) {
-  using C = DkdvCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::BLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    const bool isq = b < C::NBLK;
-    store_block<D>(t.blk[u], isq ? b : b - C::NBLK, buf + (isq ? C::OFF_QS : C::OFF_DOS), C::P,
-                   buf + (isq ? C::OFF_QT : C::OFF_DOT));
-  }
-  float* st = reinterpret_cast<float*>(buf + C::OFF_STATS);
-  if (tid < C::BQ) {
-    // log2-domain LSE; +inf past N makes P exactly 0 for rows that do not exist
-    st[tid] = q0 + tid < N ? t.stat * kLog2e : INFINITY;
-  } else if (tid < 2 * C::BQ) {
-    st[tid] = t.stat;    // delta, 0 past N
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
@@ -198,7 +110,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const rsrc_t rlse = make_rsrc(lse + (int64_t)bh * N, (uint32_t)N * 4);
   const rsrc_t rdel = make_rsrc(delta + (int64_t)bh * N, (uint32_t)N * 4);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int key = kt * C::BK + wave * 32 + li;   // this lane's key row
 
@@ -215,21 +128,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   for (int cb = 0; cb < C::DB; ++cb) dvt[cb] = dkt[cb] = zero16();
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
-  DkdvTile<D> tile;
-  dkdv_load<D>(tile, rq, rdo, rlse, rdel, 0, tid);
-  dkdv_store<D>(tile, smem, 0, N, tid);
+  // Per-row statistics of a query tile: threads 0..BQ-1 carry LSE (stored
+  // in log2 units, +inf past N so that P is exactly 0 there), threads
+  // BQ..2BQ-1 carry delta (0 past N).
+  auto load_stat = [&](int q0) -> float {
+    if (tid < 2 * C::BQ)
+      return buf_loadf(tid < C::BQ ? rlse : rdel, (uint32_t)((q0 + (tid & (C::BQ - 1))) * 4));
+    return 0.0f;
+  };
+  auto store_stat = [&](uint16_t* buf, int q0, float v) {
+    float* st = reinterpret_cast<float*>(buf + C::OFF_STATS);
+    if (tid < C::BQ)
+      st[tid] = q0 + tid < N ? v * kLog2e : INFINITY;
+    else if (tid < 2 * C::BQ)
+      st[tid] = v;
+  };
+  tile_load<D, C::BQ, C::WAVES>(smem + C::OFF_Q, rq, 0, wave, lane);
+  tile_load<D, C::BQ, C::WAVES>(smem + C::OFF_DO, rdo, 0, wave, lane);
+  store_stat(smem, 0, load_stat(0));
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < nqt; ++it) {
     const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
-    const uint16_t* Qs = buf + C::OFF_QS;
-    const uint16_t* dOs = buf + C::OFF_DOS;
-    const uint16_t* Qt = buf + C::OFF_QT;
-    const uint16_t* dOt = buf + C::OFF_DOT;
+    const uint16_t* Qs = buf + C::OFF_Q;
+    const uint16_t* dOs = buf + C::OFF_DO;
     const float* lse2s = reinterpret_cast<const float*>(buf + C::OFF_STATS);
     const float* dls = lse2s + C::BQ;
     const bool more = it + 1 < nqt;
-    if (more) dkdv_load<D>(tile, rq, rdo, rlse, rdel, (it + 1) * C::BQ, tid);
+    uint16_t* nbuf = smem + ((it + 1) & 1) * C::BUF_ELEMS;
+    float stat = 0.0f;
+    if (more) {
+      tile_load<D, C::BQ, C::WAVES>(nbuf + C::OFF_Q, rq, (it + 1) * C::BQ, wave, lane);
+      tile_load<D, C::BQ, C::WAVES>(nbuf + C::OFF_DO, rdo, (it + 1) * C::BQ, wave, lane);
+      stat = load_stat((it + 1) * C::BQ);
+    }
 
     // S = Q K^T and dP = dO V^T for the two 32-query blocks: four
     // independent accumulator chains, with the LDS operands of k-step kk+RA
@@ -237,15 +170,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     f32x16 s[2], dp[2];
     {
       constexpr int RA = kReadAhead;
-      const uint16_t* qrow = Qs + li * C::P + g * 8;
-      const uint16_t* orow = dOs + li * C::P + g * 8;
       bf16x8 qa[RA + 1][2], oa[RA + 1][2];
 #pragma unroll
       for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          qa[kk][qb] = lds_bf16x8(qrow + qb * 32 * C::P + kk * 16);
-          oa[kk][qb] = lds_bf16x8(orow + qb * 32 * C::P + kk * 16);
+          qa[kk][qb] = row_operand<D>(Qs, qb * 32 + li, 2 * kk + g);
+          oa[kk][qb] = row_operand<D>(dOs, qb * 32 + li, 2 * kk + g);
         }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
@@ -254,8 +185,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         if (kk + RA < C::DK) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            qa[(kk + RA) % (RA + 1)][qb] = lds_bf16x8(qrow + qb * 32 * C::P + (kk + RA) * 16);
-            oa[(kk + RA) % (RA + 1)][qb] = lds_bf16x8(orow + qb * 32 * C::P + (kk + RA) * 16);
+            qa[(kk + RA) % (RA + 1)][qb] = row_operand<D>(Qs, qb * 32 + li, 2 * (kk + RA) + g);
+            oa[(kk + RA) % (RA + 1)][qb] = row_operand<D>(dOs, qb * 32 + li, 2 * (kk + RA) + g);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -302,17 +233,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       bf16x8 oa[RA + 1], qa[RA + 1];
 #pragma unroll
       for (int n = 0; n < RA; ++n) {
-        const int off = tswz((n % C::DB) * 32 + li, (n / C::DB) * 16 + g * 8);
-        oa[n] = lds_bf16x8(dOt + off);
-        qa[n] = lds_bf16x8(Qt + off);
+        oa[n] = tr_operand<D>(dOs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
+        qa[n] = tr_operand<D>(Qs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
       }
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         if (n + RA < NS) {
           const int m = n + RA;
-          const int off = tswz((m % C::DB) * 32 + li, (m / C::DB) * 16 + g * 8);
-          oa[m % (RA + 1)] = lds_bf16x8(dOt + off);
-          qa[m % (RA + 1)] = lds_bf16x8(Qt + off);
+          oa[m % (RA + 1)] = tr_operand<D>(dOs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
+          qa[m % (RA + 1)] = tr_operand<D>(Qs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int t = n / C::DB, cb = n % C::DB;
@@ -321,8 +250,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
 
-    if (more) dkdv_store<D>(tile, smem + ((it + 1) & 1) * C::BUF_ELEMS, (it + 1) * C::BQ, N, tid);
-    __syncthreads();
+    if (more) store_stat(nbuf, (it + 1) * C::BQ, stat);
+    wait_vmem();      // this wave's loads of the next tile have landed
+    __syncthreads();  // ... and everyone's; the current tile is no longer read
   }
 
   // dV^T / dK^T element i of block cb: column cb*32 + 8*(i/4) + 4g + i%4 of
@@ -358,50 +288,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128, BK = 64, THREADS = 256;
-  static constexpr int P = D + 8;
-  static constexpr int ROW_ELEMS = BK * P;
-  static constexpr int T_ELEMS = D * 64;     // transposed tile (tswz layout)
-  static constexpr int OFF_KS = 0;
-  static constexpr int OFF_VS = OFF_KS + ROW_ELEMS;
-  static constexpr int OFF_KT = OFF_VS + ROW_ELEMS;
-  static constexpr int BUF_ELEMS = OFF_KT + T_ELEMS;
+  static constexpr int BQ = 128, BK = 64, WAVES = 4, THREADS = 64 * WAVES;
+  static constexpr int TILE = BK * D;          // one K or V tile (bf16), swizzled
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = TILE;
+  static constexpr int BUF_ELEMS = 2 * TILE;
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int NBLK = (BK / 4) * (D / 8);
-  static constexpr int BLK_PER_T = 2 * NBLK / THREADS;   // K and V blocks per thread
   static constexpr int DK = D / 16, DB = D / 32;
-  static_assert(BK == 64, "transposed tiles hold 64 positions per row");
-  static_assert((2 * NBLK) % THREADS == 0, "whole blocks per thread");
 };
-
-template <int D>
-struct DqTile {
-  u32x4 blk[DqCfg<D>::BLK_PER_T][4];
-};
-
-template <int D>
-__device__ __forceinline__ void dq_load(DqTile<D>& t, rsrc_t rk, rsrc_t rv, int k0, int tid) {
-  using C = DqCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::BLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    const bool isk = b < C::NBLK;
-    load_block<D>(t.blk[u], isk ? rk : rv, k0, isk ? b : b - C::NBLK);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void dq_store(const DqTile<D>& t, uint16_t* buf, int tid) {
-  using C = DqCfg<D>;
-#pragma unroll
-  for (int u = 0; u < C::BLK_PER_T; ++u) {
-    const int b = tid + u * C::THREADS;
-    if (b < C::NBLK)
-      store_block<D>(t.blk[u], b, buf + C::OFF_KS, C::P, buf + C::OFF_KT);
-    else
-      store_block<D>(t.blk[u], b - C::NBLK, buf + C::OFF_VS, C::P, nullptr);
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
@@ -421,7 +315,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const rsrc_t rq = make_rsrc(q + hoff, hbytes);
   const rsrc_t rdo = make_rsrc(dO + hoff, hbytes);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int qrow = qt * C::BQ + wave * 32 + li;
 
@@ -440,33 +335,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   for (int cb = 0; cb < C::DB; ++cb) dqt[cb] = zero16();
 
   const int nkt = (N + C::BK - 1) / C::BK;
-  DqTile<D> tile;
-  dq_load<D>(tile, rk, rv, 0, tid);
-  dq_store<D>(tile, smem, tid);
+  tile_load<D, C::BK, C::WAVES>(smem + C::OFF_K, rk, 0, wave, lane);
+  tile_load<D, C::BK, C::WAVES>(smem + C::OFF_V, rv, 0, wave, lane);
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < nkt; ++it) {
     const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
-    const uint16_t* Ks = buf + C::OFF_KS;
-    const uint16_t* Vs = buf + C::OFF_VS;
-    const uint16_t* Kt = buf + C::OFF_KT;
-    const bool more = it + 1 < nkt;
-    if (more) dq_load<D>(tile, rk, rv, (it + 1) * C::BK, tid);
+    const uint16_t* Ks = buf + C::OFF_K;
+    const uint16_t* Vs = buf + C::OFF_V;
+    if (it + 1 < nkt) {
+      uint16_t* nbuf = smem + ((it + 1) & 1) * C::BUF_ELEMS;
+      tile_load<D, C::BK, C::WAVES>(nbuf + C::OFF_K, rk, (it + 1) * C::BK, wave, lane);
+      tile_load<D, C::BK, C::WAVES>(nbuf + C::OFF_V, rv, (it + 1) * C::BK, wave, lane);
+    }
 
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks, operands
     // read kReadAhead k-steps ahead.
     f32x16 s[2], dp[2];
     {
       constexpr int RA = kReadAhead;
-      const uint16_t* krow = Ks + li * C::P + g * 8;
-      const uint16_t* vrow = Vs + li * C::P + g * 8;
       bf16x8 ka[RA + 1][2], va[RA + 1][2];
 #pragma unroll
       for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          ka[kk][kb] = lds_bf16x8(krow + kb * 32 * C::P + kk * 16);
-          va[kk][kb] = lds_bf16x8(vrow + kb * 32 * C::P + kk * 16);
+          ka[kk][kb] = row_operand<D>(Ks, kb * 32 + li, 2 * kk + g);
+          va[kk][kb] = row_operand<D>(Vs, kb * 32 + li, 2 * kk + g);
         }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = zero16();
@@ -475,8 +370,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         if (kk + RA < C::DK) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            ka[(kk + RA) % (RA + 1)][kb] = lds_bf16x8(krow + kb * 32 * C::P + (kk + RA) * 16);
-            va[(kk + RA) % (RA + 1)][kb] = lds_bf16x8(vrow + kb * 32 * C::P + (kk + RA) * 16);
+            ka[(kk + RA) % (RA + 1)][kb] = row_operand<D>(Ks, kb * 32 + li, 2 * (kk + RA) + g);
+            va[(kk + RA) % (RA + 1)][kb] = row_operand<D>(Vs, kb * 32 + li, 2 * (kk + RA) + g);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -509,13 +404,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       constexpr int RA = kStepAhead, NS = (C::BK / 16) * C::DB;
       bf16x8 ka[RA + 1];
 #pragma unroll
-      for (int n = 0; n < RA; ++n)
-        ka[n] = lds_bf16x8(Kt + tswz((n % C::DB) * 32 + li, (n / C::DB) * 16 + g * 8));
+      for (int n = 0; n < RA; ++n) ka[n] = tr_operand<D>(Ks, (n / C::DB) * 16, (n % C::DB) * 32, lane);
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         if (n + RA < NS) {
           const int m = n + RA;
-          ka[m % (RA + 1)] = lds_bf16x8(Kt + tswz((m % C::DB) * 32 + li, (m / C::DB) * 16 + g * 8));
+          ka[m % (RA + 1)] = tr_operand<D>(Ks, (m / C::DB) * 16, (m % C::DB) * 32, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int cb = n % C::DB;
@@ -523,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       }
     }
 
-    if (more) dq_store<D>(tile, smem + ((it + 1) & 1) * C::BUF_ELEMS, tid);
+    wait_vmem();
     __syncthreads();
   }
 

@@ -3,15 +3,19 @@
 //
 // Layout.  A tile holds rows of D bf16 values (2*D bytes, no padding).  Each
 // row is a sequence of 16-byte chunks; logical chunk c of row r is stored at
-// physical chunk c ^ swz(r), swz(r) = 2*(r & 3) + ((r >> 2) & 1) (a 3-bit
-// XOR, so a chunk never leaves its group of eight).  Two read patterns are
-// then free of LDS bank conflicts:
-//   - 8 consecutive rows, same logical chunk (matrix-core operand rows):
-//     swz takes 8 distinct values on any 8 consecutive rows;
-//   - 4 consecutive rows starting at a multiple of 4, two adjacent chunks
-//     (the transposing reads): swz takes the values {0,2,4,6} + b there, so
-//     the four chunk pairs land on four distinct pairs.
-//
+// physical chunk c ^ swz<D>(r).  LDS has 64 banks of 4 bytes; a 16-byte
+// read is served 16 lanes at a time and an 8-byte read 32 lanes at a time,
+// so the swizzle is chosen to make both read patterns conflict-free:
+//   - row operands: 16 consecutive rows, one logical chunk each.  With
+//     D = 128 a row spans all 64 banks and the bank group is the physical
+//     chunk, so swz must take 16 distinct values on 16 consecutive rows;
+//     with D = 64 two rows share the banks (row parity picks the half), so
+//     swz must be distinct on the 8 rows of each parity.
+//   - transposed operands: 4 consecutive rows (from a multiple of 4), the 4
+//     chunks of one 32-column block each: the 4 rows (per parity, D = 64)
+//     must land on different 4-chunk blocks.
+//   D = 128: swz(r) = 4 (r & 3) + ((r >> 2) & 3)
+//   D = 64:  swz(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)
 // Loads.  A direct buffer->LDS load writes lane L's 16 bytes at LDS address
 // M0 + 16 L whatever global address the lane read, so the swizzle is applied
 // on the global side: the lane that fills physical chunk p of row r reads
@@ -34,12 +38,16 @@ namespace fa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "tile widths of 64 or 128 bf16");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // Offset (bf16 elements) of logical chunk c of row r in a tile with D columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * D + ((c ^ swz(r)) << 3);
+  return r * D + ((c ^ swz<D>(r)) << 3);
 }
 
 // LDS byte address of a pointer into shared memory.
@@ -79,7 +87,7 @@ __device__ __forceinline__ void tile_load(uint16_t* tile, rsrc_t src, int r0, in
     const int i = wave + u * NW;
     const int lin = i * 64 + lane;         // physical chunk position in the tile
     const int row = lin / NC, phys = lin % NC;
-    const int c = phys ^ swz(row);
+    const int c = phys ^ swz<D>(row);
     const uint32_t off = (uint32_t)(((r0 + row) * D + c * 8) * 2);
     lds_dma16(src, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + i * 64 * 8)));
   }
