@@ -164,89 +164,77 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       stat = load_stat((it + 1) * C::BQ);
     }
 
-    // S = Q K^T and dP = dO V^T for the two 32-query blocks: four
-    // independent accumulator chains, with the LDS operands of k-step kk+RA
-    // read before the instructions of step kk (see kReadAhead).
-    f32x16 s[2], dp[2];
-    {
-      constexpr int RA = kReadAhead;
-      bf16x8 qa[RA + 1][2], oa[RA + 1][2];
+    // One 32-query block at a time: S = Q K^T and dP = dO V^T (operands
+    // read kReadAhead k-steps ahead), then P and dS, then dV^T += dO^T P and
+    // dK^T += Q^T dS for the block's two 16-query steps (dO^T and Q^T
+    // gathered with transposing reads kStepAhead steps ahead).
 #pragma unroll
-      for (int kk = 0; kk < RA; ++kk)
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s = zero16(), dp = zero16();
+      {
+        constexpr int RA = kReadAhead;
+        bf16x8 qa[RA + 1], oa[RA + 1];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          qa[kk][qb] = row_operand<D>(Qs, qb * 32 + li, 2 * kk + g);
-          oa[kk][qb] = row_operand<D>(dOs, qb * 32 + li, 2 * kk + g);
+        for (int kk = 0; kk < RA; ++kk) {
+          qa[kk] = row_operand<D>(Qs, qb * 32 + li, 2 * kk + g);
+          oa[kk] = row_operand<D>(dOs, qb * 32 + li, 2 * kk + g);
         }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) {
-        if (kk + RA < C::DK) {
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            qa[(kk + RA) % (RA + 1)][qb] = row_operand<D>(Qs, qb * 32 + li, 2 * (kk + RA) + g);
-            oa[(kk + RA) % (RA + 1)][qb] = row_operand<D>(dOs, qb * 32 + li, 2 * (kk + RA) + g);
+        for (int kk = 0; kk < C::DK; ++kk) {
+          if (kk + RA < C::DK) {
+            qa[(kk + RA) % (RA + 1)] = row_operand<D>(Qs, qb * 32 + li, 2 * (kk + RA) + g);
+            oa[(kk + RA) % (RA + 1)] = row_operand<D>(dOs, qb * 32 + li, 2 * (kk + RA) + g);
           }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = mfma32(qa[kk % (RA + 1)][qb], kreg[kk], s[qb]);
-          dp[qb] = mfma32(oa[kk % (RA + 1)][qb], vreg[kk], dp[qb]);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32(qa[kk % (RA + 1)], kreg[kk], s);
+          dp = mfma32(oa[kk % (RA + 1)], vreg[kk], dp);
         }
       }
-    }
-    // P and dS; element i of block qb is query qb*32 + 8*(i/4) + 4g + i%4.
+      // P and dS; element 4r + e is query qb*32 + 8r + 4g + e.
+      bf16x8 pb[2], sb[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pw, sw;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qo = qb * 32 + 8 * r + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qo);
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = 2 * h + rr;
+          const int qo = qb * 32 + 8 * r + 4 * g;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qo);
+          float p[4], d[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(fmaf(s[qb][4 * r + e], c2, -l4[e]));
-          s[qb][4 * r + e] = p;
-          dp[qb][4 * r + e] = p * (dp[qb][4 * r + e] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            p[e] = fast_exp2(fmaf(s[4 * r + e], c2, -l4[e]));
+            d[e] = p[e] * (dp[4 * r + e] - d4[e]);
+          }
+          pw[2 * rr] = pack_bf16x2(p[0], p[1]);
+          pw[2 * rr + 1] = pack_bf16x2(p[2], p[3]);
+          sw[2 * rr] = pack_bf16x2(d[0], d[1]);
+          sw[2 * rr + 1] = pack_bf16x2(d[2], d[3]);
         }
+        pb[h] = as_bf16x8(pw);
+        sb[h] = as_bf16x8(sw);
       }
-    // P and dS to bf16 B operands, one per 16-query step t.
-    bf16x8 pb[C::BQ / 16], sb[C::BQ / 16];
+      {
+        constexpr int SA = kStepAhead, NS = 2 * C::DB;   // steps n = (h, cb)
+        bf16x8 oa[SA + 1], qa[SA + 1];
 #pragma unroll
-    for (int t = 0; t < C::BQ / 16; ++t) {
-      const int qb = t >> 1, h = t & 1;
-      u32x4 pw, sw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pw[e] = pack_bf16x2(s[qb][8 * h + 2 * e], s[qb][8 * h + 2 * e + 1]);
-        sw[e] = pack_bf16x2(dp[qb][8 * h + 2 * e], dp[qb][8 * h + 2 * e + 1]);
-      }
-      pb[t] = as_bf16x8(pw);
-      sb[t] = as_bf16x8(sw);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over steps n = (t, cb), operands
-    // read kStepAhead steps ahead.
-    {
-      constexpr int RA = kStepAhead, NS = (C::BQ / 16) * C::DB;
-      bf16x8 oa[RA + 1], qa[RA + 1];
-#pragma unroll
-      for (int n = 0; n < RA; ++n) {
-        oa[n] = tr_operand<D>(dOs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
-        qa[n] = tr_operand<D>(Qs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
-      }
-#pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        if (n + RA < NS) {
-          const int m = n + RA;
-          oa[m % (RA + 1)] = tr_operand<D>(dOs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
-          qa[m % (RA + 1)] = tr_operand<D>(Qs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
+        for (int n = 0; n < SA; ++n) {
+          oa[n] = tr_operand<D>(dOs, (2 * qb + n / C::DB) * 16, (n % C::DB) * 32, lane);
+          qa[n] = tr_operand<D>(Qs, (2 * qb + n / C::DB) * 16, (n % C::DB) * 32, lane);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        const int t = n / C::DB, cb = n % C::DB;
-        dvt[cb] = mfma32(oa[n % (RA + 1)], pb[t], dvt[cb]);
-        dkt[cb] = mfma32(qa[n % (RA + 1)], sb[t], dkt[cb]);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          if (n + SA < NS) {
+            const int m = n + SA;
+            oa[m % (SA + 1)] = tr_operand<D>(dOs, (2 * qb + m / C::DB) * 16, (m % C::DB) * 32, lane);
+            qa[m % (SA + 1)] = tr_operand<D>(Qs, (2 * qb + m / C::DB) * 16, (m % C::DB) * 32, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const int h = n / C::DB, cb = n % C::DB;
+          dvt[cb] = mfma32(oa[n % (SA + 1)], pb[h], dvt[cb]);
+          dkt[cb] = mfma32(qa[n % (SA + 1)], sb[h], dkt[cb]);
+        }
       }
     }
 
@@ -298,7 +286,7 @@ struct DqCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta,
@@ -350,70 +338,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       tile_load<D, C::BK, C::WAVES>(nbuf + C::OFF_V, rv, (it + 1) * C::BK, wave, lane);
     }
 
-    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks, operands
-    // read kReadAhead k-steps ahead.
-    f32x16 s[2], dp[2];
-    {
-      constexpr int RA = kReadAhead;
-      bf16x8 ka[RA + 1][2], va[RA + 1][2];
+    // One 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (operands
+    // read kReadAhead k-steps ahead), then P^T and dS^T for this lane's
+    // query, then dQ^T += K^T dS^T for the block's two 16-key steps (K^T
+    // gathered with transposing reads kStepAhead steps ahead).  Only one
+    // block's scores are live at a time.
 #pragma unroll
-      for (int kk = 0; kk < RA; ++kk)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = zero16(), dp = zero16();
+      {
+        constexpr int RA = kReadAhead;
+        bf16x8 ka[RA + 1], va[RA + 1];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          ka[kk][kb] = row_operand<D>(Ks, kb * 32 + li, 2 * kk + g);
-          va[kk][kb] = row_operand<D>(Vs, kb * 32 + li, 2 * kk + g);
+        for (int kk = 0; kk < RA; ++kk) {
+          ka[kk] = row_operand<D>(Ks, kb * 32 + li, 2 * kk + g);
+          va[kk] = row_operand<D>(Vs, kb * 32 + li, 2 * kk + g);
         }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) {
-        if (kk + RA < C::DK) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            ka[(kk + RA) % (RA + 1)][kb] = row_operand<D>(Ks, kb * 32 + li, 2 * (kk + RA) + g);
-            va[(kk + RA) % (RA + 1)][kb] = row_operand<D>(Vs, kb * 32 + li, 2 * (kk + RA) + g);
+        for (int kk = 0; kk < C::DK; ++kk) {
+          if (kk + RA < C::DK) {
+            ka[(kk + RA) % (RA + 1)] = row_operand<D>(Ks, kb * 32 + li, 2 * (kk + RA) + g);
+            va[(kk + RA) % (RA + 1)] = row_operand<D>(Vs, kb * 32 + li, 2 * (kk + RA) + g);
           }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = mfma32(ka[kk % (RA + 1)][kb], qreg[kk], s[kb]);
-          dp[kb] = mfma32(va[kk % (RA + 1)][kb], oreg[kk], dp[kb]);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32(ka[kk % (RA + 1)], qreg[kk], s);
+          dp = mfma32(va[kk % (RA + 1)], oreg[kk], dp);
         }
       }
-    }
+      bf16x8 sb[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int h = 0; h < 2; ++h) {
+        u32x4 sw;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[kb][i], c2, -lse2));
-        dp[kb][i] = p * (dp[kb][i] - dl);
-      }
-    bf16x8 sb[C::BK / 16];
-#pragma unroll
-    for (int t = 0; t < C::BK / 16; ++t) {
-      const int kb = t >> 1, h = t & 1;
-      u32x4 sw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sw[e] = pack_bf16x2(dp[kb][8 * h + 2 * e], dp[kb][8 * h + 2 * e + 1]);
-      sb[t] = as_bf16x8(sw);
-    }
-    // dQ^T += K^T dS^T over steps n = (t, cb), operands read kStepAhead
-    // steps ahead.
-    {
-      constexpr int RA = kStepAhead, NS = (C::BK / 16) * C::DB;
-      bf16x8 ka[RA + 1];
-#pragma unroll
-      for (int n = 0; n < RA; ++n) ka[n] = tr_operand<D>(Ks, (n / C::DB) * 16, (n % C::DB) * 32, lane);
-#pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        if (n + RA < NS) {
-          const int m = n + RA;
-          ka[m % (RA + 1)] = tr_operand<D>(Ks, (m / C::DB) * 16, (m % C::DB) * 32, lane);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[8 * h + 2 * e], c2, -lse2));
+          const float p1 = fast_exp2(fmaf(s[8 * h + 2 * e + 1], c2, -lse2));
+          sw[e] = pack_bf16x2(p0 * (dp[8 * h + 2 * e] - dl), p1 * (dp[8 * h + 2 * e + 1] - dl));
         }
-        __builtin_amdgcn_sched_barrier(0);
-        const int cb = n % C::DB;
-        dqt[cb] = mfma32(ka[n % (RA + 1)], sb[n / C::DB], dqt[cb]);
+        sb[h] = as_bf16x8(sw);
+      }
+      {
+        constexpr int SA = kStepAhead, NS = 2 * C::DB;   // steps n = (h, cb)
+        bf16x8 ka[SA + 1];
+#pragma unroll
+        for (int n = 0; n < SA; ++n)
+          ka[n] = tr_operand<D>(Ks, (2 * kb + n / C::DB) * 16, (n % C::DB) * 32, lane);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          if (n + SA < NS) {
+            const int m = n + SA;
+            ka[m % (SA + 1)] = tr_operand<D>(Ks, (2 * kb + m / C::DB) * 16, (m % C::DB) * 32, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const int cb = n % C::DB;
+          dqt[cb] = mfma32(ka[n % (SA + 1)], sb[n / C::DB], dqt[cb]);
+        }
       }
     }
 
