@@ -12,7 +12,7 @@
 //   the only values written back (算珠楼的掌簿人, 技术解读).
 //
 // Work decomposition:
-//   workgroup = 4 waves; each wave owns QB blocks of 32 query rows of one
+//   workgroup = NWAVES waves; each wave owns QB blocks of 32 query rows of one
 //   (batch, head).  Key tiles of BC rows stream through LDS, double-buffered:
 //   direct buffer->LDS loads of tile j+1 are issued at the start of tile j
 //   (no registers involved), one barrier per tile.  With QB = 2 every K and V
@@ -23,8 +23,10 @@
 //   sit in lane l^32).  The row max and row sum are in-lane reductions plus
 //   one exchange between the two half-waves.  The probabilities leave the
 //   score accumulators already in the B-operand layout of O^T += V^T P^T, so
-//   P never touches LDS; the V^T operand is gathered from the row-major V
-//   tile with transposing LDS reads in the matching key order (lds_tile.h).
+//   P never touches LDS; the V^T operand is gathered from the V tile with
+//   transposing LDS reads in the matching key order.  Both tiles are stored
+//   in the order their reads consume them (lds_tile.h), so every LDS read is
+//   a base register plus an immediate offset.
 //   Base-2 domain: c = scale * log2(e); p = 2^(c s - m) with m in log2 units;
 //   LSE = ln 2 * (m + log2 l).
 #include "lds_tile.h"
@@ -39,9 +41,9 @@ constexpr float kSlack = 8.0f;
 constexpr int kReadAhead = 2;
 constexpr int kStepAhead = 4;
 
-template <int D, int QB, int BC>
+template <int D, int QB, int BC, int NWAVES = 4>
 struct FwdCfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = NWAVES;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = WAVES * 32 * QB;      // query rows per workgroup
   static constexpr int KB = BC / 32;              // 32-key blocks per tile
@@ -63,12 +65,12 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return x * base + (x < rem ? x : rem) + idx;
 }
 
-template <int D, int QB, int BC, int MINW, bool PRIO>
-__global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
+template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4>
+__global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int N,
     int ntq, float c2) {
-  using C = FwdCfg<D, QB, BC>;
+  using C = FwdCfg<D, QB, BC, NWAVES>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -108,18 +110,18 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
   }
 
   const int nkt = (N + BC - 1) / BC;
-  tile_load<D, BC, C::WAVES>(smem, rk, 0, wave, lane);
-  tile_load<D, BC, C::WAVES>(smem + C::TILE, rv, 0, wave, lane);
+  rowop_load<D, BC, C::WAVES>(smem, rk, 0, wave, lane);
+  trop_load<D, BC, C::WAVES>(smem + C::TILE, rv, 0, wave, lane);
   wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < nkt; ++j) {
-    const uint16_t* ks = smem + (j & 1) * C::BUF_ELEMS;
-    const uint16_t* vs = ks + C::TILE;
+    const uint16_t* kl = smem + (j & 1) * C::BUF_ELEMS + 8 * lane;   // this lane's K reads
+    const uint16_t* vl = smem + (j & 1) * C::BUF_ELEMS + C::TILE + 4 * lane;
     if (j + 1 < nkt) {
       uint16_t* nb = smem + ((j + 1) & 1) * C::BUF_ELEMS;
-      tile_load<D, BC, C::WAVES>(nb, rk, (j + 1) * BC, wave, lane);
-      tile_load<D, BC, C::WAVES>(nb + C::TILE, rv, (j + 1) * BC, wave, lane);
+      rowop_load<D, BC, C::WAVES>(nb, rk, (j + 1) * BC, wave, lane);
+      trop_load<D, BC, C::WAVES>(nb + C::TILE, rv, (j + 1) * BC, wave, lane);
     }
 
     // S^T = K_j Q^T in 32-key blocks; A = K rows from LDS (each read feeds
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) kop[kk][kb] = row_operand<D>(ks, kb * 32 + li, 2 * kk + g);
+      for (int kb = 0; kb < C::KB; ++kb) kop[kk][kb] = rowop_read<D>(kl, kb, kk);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
       if (kk + RA < C::DK) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
-          kop[(kk + RA) % (RA + 1)][kb] = row_operand<D>(ks, kb * 32 + li, 2 * (kk + RA) + g);
+          kop[(kk + RA) % (RA + 1)][kb] = rowop_read<D>(kl, kb, kk + RA);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -224,12 +226,12 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
       constexpr int SA = kStepAhead, NS = (BC / 16) * C::DB;
       bf16x8 vop[SA + 1];
 #pragma unroll
-      for (int n = 0; n < SA; ++n) vop[n] = tr_operand<D>(vs, (n / C::DB) * 16, (n % C::DB) * 32, lane);
+      for (int n = 0; n < SA; ++n) vop[n] = trop_read<D>(vl, n / C::DB, n % C::DB);
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         if (n + SA < NS) {
           const int m = n + SA;
-          vop[m % (SA + 1)] = tr_operand<D>(vs, (m / C::DB) * 16, (m % C::DB) * 32, lane);
+          vop[m % (SA + 1)] = trop_read<D>(vl, m / C::DB, m % C::DB);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int t = n / C::DB, db = n % C::DB;
@@ -265,13 +267,13 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int QB, int BC, int MINW, bool PRIO>
+template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4>
 int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
            int64_t BH, int64_t N, float scale, hipStream_t stream) {
-  using C = FwdCfg<D, QB, BC>;
+  using C = FwdCfg<D, QB, BC, NWAVES>;
   const int ntq = (int)((N + C::BR - 1) / C::BR);
   const int64_t nwg = (int64_t)ntq * BH;
-  auto kern = fwd_bf16_kernel<D, QB, BC, MINW, PRIO>;
+  auto kern = fwd_bf16_kernel<D, QB, BC, MINW, PRIO, NWAVES>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
@@ -288,8 +290,11 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   const auto* k16 = static_cast<const uint16_t*>(k);
   const auto* v16 = static_cast<const uint16_t*>(v);
   auto* o16 = static_cast<uint16_t*>(o);
-  if (d == 128) return launch<128, 1, 64, 2, false>(q16, k16, v16, o16, lse, BH, N, scale, stream);
-  return launch<64, 1, 64, 2, false>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+  // d = 128: 8 waves x 32 query rows, key tiles of 128 (one workgroup per CU,
+  // two waves per SIMD); d = 64: 4 waves x 32 rows, key tiles of 64.
+  if (d == 128)
+    return launch<128, 1, 128, 2, true, 8>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+  return launch<64, 1, 64, 2, false, 4>(q16, k16, v16, o16, lse, BH, N, scale, stream);
 }
 
 }  // namespace fa

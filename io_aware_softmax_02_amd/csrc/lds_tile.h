@@ -60,15 +60,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // so that the compiler does not order later LDS reads of *other* buffers
 // behind it; completion is awaited explicitly (wait_vmem) before the barrier
 // that publishes the tile.  M0 is saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t lds) {
+// The byte offset is voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t lds,
+                                          uint32_t soff = 0) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(r), "s"(lds)
+      : "v"(voff), "s"(r), "s"(lds), "s"(soff)
       : "memory");
 }
 
@@ -88,8 +90,9 @@ __device__ __forceinline__ void tile_load(uint16_t* tile, rsrc_t src, int r0, in
     const int lin = i * 64 + lane;         // physical chunk position in the tile
     const int row = lin / NC, phys = lin % NC;
     const int c = phys ^ swz<D>(row);
-    const uint32_t off = (uint32_t)(((r0 + row) * D + c * 8) * 2);
-    lds_dma16(src, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + i * 64 * 8)));
+    const uint32_t off = (uint32_t)((row * D + c * 8) * 2);
+    lds_dma16(src, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + i * 64 * 8)),
+              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
   }
 }
 
@@ -114,6 +117,73 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int rb, int c
       (__attribute__((address_space(3))) s16x4*)(p1));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p2));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
+  return as_bf16x8(w);
+}
+
+// ---------------------------------------------------------------------------
+// Operand-ordered tiles.  When a tile is only ever read one way, it can be
+// stored in the order the reads consume it: every read is then one base
+// register plus an immediate offset (no per-read address arithmetic), and
+// consecutive lanes read consecutive bytes (no bank conflicts).  R rows of D
+// bf16 values.
+//
+// Row-operand order: block (kb, kk) (kb < R/32, kk < D/16), 1 KB, holds for
+// lane L the 8 values K[kb*32 + L%32][(2 kk + L/32) * 8 ..] at byte 16 L,
+// i.e. exactly a matrix-core A/B operand.  One direct load per block.
+template <int D, int R, int NW>
+__device__ __forceinline__ void rowop_load(uint16_t* tile, rsrc_t src, int r0, int wave,
+                                           int lane) {
+  constexpr int DK = D / 16, NB = (R / 32) * DK;
+  static_assert(NB % NW == 0, "the same number of instructions for every wave");
+#pragma unroll
+  for (int u = 0; u < NB / NW; ++u) {
+    const int b = wave + u * NW, kb = b / DK, kk = b % DK;
+    const int row = kb * 32 + (lane & 31), col = (2 * kk + (lane >> 5)) * 8;
+    lds_dma16(src, (uint32_t)((row * D + col) * 2),
+              __builtin_amdgcn_readfirstlane(lds_addr(tile + b * 512)),
+              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
+  }
+}
+// The operand of block (kb, kk) for this lane: `lanebase` = tile + 8 * lane.
+template <int D>
+__device__ __forceinline__ bf16x8 rowop_read(const uint16_t* lanebase, int kb, int kk) {
+  return lds_bf16x8(lanebase + (kb * (D / 16) + kk) * 512);
+}
+
+// Transposing-read order: for 16-row step t (< R/16), 32-column block cb
+// (< D/32) and half h (0, 1), a 512-byte block holds at byte 8 s the source
+// lane s = 16 q + 4 a + b of a ds_read_b64_tr_b16: values
+// M[16 t + 8 h + 4 (q >> 1) + a][32 cb + 16 (q & 1) + 4 b ..+3].  The two
+// halves of (t, cb) are adjacent, and the 16 bytes a direct-load lane writes
+// (slots 2L, 2L + 1 of a 1 KB pair) are 8 consecutive values of one row.
+template <int D, int R, int NW>
+__device__ __forceinline__ void trop_load(uint16_t* tile, rsrc_t src, int r0, int wave,
+                                          int lane) {
+  constexpr int DB = D / 32, NP = (R / 16) * DB;    // 1 KB block pairs
+  static_assert(NP % NW == 0, "the same number of instructions for every wave");
+  const int h = lane >> 5, s = 2 * (lane & 31);
+  const int q = s >> 4, a = (s >> 2) & 3, b = s & 3;
+#pragma unroll
+  for (int u = 0; u < NP / NW; ++u) {
+    const int pidx = wave + u * NW, t = pidx / DB, cb = pidx % DB;
+    const int row = 16 * t + 8 * h + 4 * (q >> 1) + a;
+    const int col = 32 * cb + 16 * (q & 1) + 4 * b;
+    lds_dma16(src, (uint32_t)((row * D + col) * 2),
+              __builtin_amdgcn_readfirstlane(lds_addr(tile + pidx * 512)),
+              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
+  }
+}
+// Transposed operand (same values and order as tr_operand) of step t, block
+// cb for this lane: `lanebase` = tile + 4 * lane.
+template <int D>
+__device__ __forceinline__ bf16x8 trop_read(const uint16_t* lanebase, int t, int cb) {
+  const uint16_t* p = lanebase + (t * (D / 32) + cb) * 512;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p + 256));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
   return as_bf16x8(w);
