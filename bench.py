@@ -30,6 +30,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 METRIC = "attention TFLOP/s fwd & fwd+bwd, % of bf16 MFMA peak, N=8192 d=128"
 WORKLOAD = "attn_bf16_b1h16_n8192_d128_fwdbwd"
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+# (scaled by the same counters on the calibration copy), with the SHA-256 of
+# the sources and build script the kernels were built from; reported only
+# while those files are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_b1h16_n8192_d128_hbm_traffic.json")
 
 
 def parse():
@@ -54,6 +59,24 @@ def time_launches(fn, n, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per launch of `kernel`, or None if not measured
+    for the current sources."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    for rel, digest in rec["source_sha256"].items():
+        try:
+            cur = hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()
+        except OSError:
+            return None
+        if cur != digest:
+            return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(w, heads):
@@ -207,7 +230,8 @@ def main():
         "mem_inputs_outputs_bytes": int(mem_base),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom), "traffic_unit": "HBM bytes per launch"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
