@@ -33,6 +33,8 @@ namespace {
 // per instruction.
 constexpr int kReadAhead = 2;
 constexpr int kStepAhead = 4;
+constexpr int kDkdvStepAhead = 4;
+constexpr int kDkdvReadAhead = 3;
 
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   const int x = wg & 7, idx = wg >> 3;
@@ -69,24 +71,48 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------
 // dK / dV: workgroup owns 128 keys (4 waves x 32), loops over 64-query tiles.
-// Per wave and tile (lane l: key l%32 of the wave's block, k-group g):
-//   S  = Q K^T     (rows = queries, cols = keys; A = Q rows from LDS, B = K regs)
-//   dP = dO V^T    (A = dO rows from LDS, B = V regs)
-//   P  = 2^(c S - LSE log2 e), dS = P (dP - D)        (per-element, fp32)
-//   dV^T += dO^T P (A = dO^T from LDS, B = P from the S accumulators)
-//   dK^T += Q^T dS (A = Q^T from LDS,  B = dS)
+// Per wave and 32-query block j (lane l: key l%32 of the wave's block, k-group g):
+//   A(j): S  = Q K^T  (rows = queries, cols = keys; A = Q rows from LDS, B = K regs)
+//         dP = dO V^T (A = dO rows from LDS, B = V regs)
+//   B(j): P  = 2^(c S'), dS = P dP'                          (per-element, fp32)
+// where S' = S - LSE/s and dP' = dP - D come out of the contractions directly
+// (c = s log2 e): each contraction has one more k-step whose A operand holds
+// -LSE/s (resp. -D) of the lane's query row split exactly into three bf16
+// parts (8 + 8 + 8 significand bits) and whose B operand is (1, 1, 1, 0, ..).
+// That step is issued last, so its operand is built while the others run.
+// Query rows past N read as zero rows of Q and dO with LSE = D = 0, so their
+// P is 1 but multiplies a zero row of dO, and their dS is 0.
+//   C(j): dV^T += dO^T P (A = dO^T from LDS, B = P from the S accumulators)
+//         dK^T += Q^T dS (A = Q^T from LDS,  B = dS)
+// Software pipeline: the vector work B(j) runs between the matrix-core
+// instructions of C(j-1) (P and dS of two blocks alternate), so the order is
+// A(j), B(j) | C(j-1), A(j+1), B(j+1) | C(j), ...  B itself is split in two
+// stages (scale + exp, then multiply + pack) that are one C step apart, so
+// that no vector instruction between two matrix-core instructions waits on
+// another.  K and V stay in accumulation registers, which the matrix cores
+// read directly.
+// Tiles are triple-buffered with one barrier per tile, three C steps before
+// the first A of the tile it publishes (the A's first operands are read
+// right after it); the loads of the tile after next are issued one
+// instruction at a time between the matrix-core instructions of the A phases,
+// into the buffer whose last reader (a C phase) finished before the barrier.
+// Loads past the last tile read as zeros and only feed A and B work that no
+// C consumes.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
-  static constexpr int BK = 128, BQ = 64, WAVES = 4, THREADS = 64 * WAVES;
-  static constexpr int TILE = BQ * D;          // one Q or dO tile (bf16), swizzled
-  // One buffer: Q tile, dO tile, lse2[BQ], delta[BQ]
+  static constexpr int BK = 128, BQ = 64, WAVES = 4, THREADS = 64 * WAVES, NBUF = 3;
+  static constexpr int TILE = BQ * D;          // one 64-row tile of Q or dO (bf16), swizzled
+  // One buffer: Q tile, dO tile, LSE [BQ], delta [BQ] (fp32), and a spare
+  // copy of both (waves 2 and 3 load it so that no wave branches).
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = TILE;
   static constexpr int OFF_STATS = 2 * TILE;   // bf16 units; 2*BQ floats follow
-  static constexpr int BUF_ELEMS = OFF_STATS + 4 * BQ;
-  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int DK = D / 16, DB = D / 32;
+  static constexpr int BUF_ELEMS = OFF_STATS + 8 * BQ;
+  static constexpr int LDS_BYTES = NBUF * BUF_ELEMS * 2;
+  static constexpr int DK = D / 16, DB = D / 32, NS = 2 * DB;
+  static constexpr int NIW = TILE / 512 / WAVES;   // 1 KB loads per wave per tensor tile
+  static_assert(DK == 2 * NIW && NS == DK, "one load every other k-step; B fits C's steps");
 };
 
 template <int D>
@@ -97,6 +123,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int nkt, float c2,
     float scale) {
   using C = DkdvCfg<D>;
+  constexpr int DK = C::DK, DB = C::DB, NS = C::NS, NIW = C::NIW;
+  constexpr int RA = kDkdvReadAhead, SA = kDkdvStepAhead;
+  constexpr int HPS = 8 / NS;                  // half-parts of B per step of C
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -112,136 +141,271 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 31, g = lane >> 5;
-  const int key = kt * C::BK + wave * 32 + li;   // this lane's key row
+  const int g = lane >> 5;
+  const int key = kt * C::BK + wave * 32 + (lane & 31);   // this lane's key row
 
-  // K and V rows of this lane's key as B operands (k-step kk: cols kk*16+8g..).
-  bf16x8 kreg[C::DK], vreg[C::DK];
+  // K and V rows of this lane's key as B operands (k-step kk: cols kk*16+8g..),
+  // kept in accumulation registers (all loads are issued before any is used).
+  bf16x8 kreg[DK], vreg[DK];
 #pragma unroll
-  for (int kk = 0; kk < C::DK; ++kk) {
+  for (int kk = 0; kk < DK; ++kk) {
     const uint32_t off = (uint32_t)((key * D + kk * 16 + g * 8) * 2);
     kreg[kk] = as_bf16x8(buf_load16(rk, off));
     vreg[kk] = as_bf16x8(buf_load16(rv, off));
   }
-  f32x16 dvt[C::DB], dkt[C::DB];
 #pragma unroll
-  for (int cb = 0; cb < C::DB; ++cb) dvt[cb] = dkt[cb] = zero16();
+  for (int kk = 0; kk < DK; ++kk) {
+    asm volatile("" : "+a"(kreg[kk]));
+    asm volatile("" : "+a"(vreg[kk]));
+  }
+  f32x16 dvt[DB], dkt[DB];
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) dvt[cb] = dkt[cb] = zero16();
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
-  // Per-row statistics of a query tile: threads 0..BQ-1 carry LSE (stored
-  // in log2 units, +inf past N so that P is exactly 0 there), threads
-  // BQ..2BQ-1 carry delta (0 past N).
-  auto load_stat = [&](int q0) -> float {
-    if (tid < 2 * C::BQ)
-      return buf_loadf(tid < C::BQ ? rlse : rdel, (uint32_t)((q0 + (tid & (C::BQ - 1))) * 4));
-    return 0.0f;
+  const float neg_inv_scale = -1.0f / scale;
+  // Load m (0 .. 2 NIW - 1) of this wave's share of tile `t` into buffer b;
+  // with m == 0 each wave also loads the tile's LSE (even waves) or delta
+  // (odd waves) row, waves 2 and 3 into the spare copy.
+  static_assert(C::BQ == 64, "one wave per statistic");
+  const uint32_t dvoff = tile_dma_voff<D, C::WAVES>(wave, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  auto dma = [&](int b, int t, int m) {
+    const int tensor = m / NIW;
+    tile_dma<D, C::WAVES>(lds0 + (uint32_t)((b * C::BUF_ELEMS + tensor * C::TILE) * 2),
+                          tensor ? rdo : rq, dvoff, (uint32_t)(t * C::BQ * D * 2), wave, m % NIW);
+    if (m == 0)
+      lds_dma4((wave & 1) ? rdel : rlse, (uint32_t)(lane * 4),
+               lds0 + (uint32_t)((b * C::BUF_ELEMS + C::OFF_STATS) * 2 + wave * C::BQ * 4),
+               (uint32_t)(t * C::BQ * 4));
   };
-  auto store_stat = [&](uint16_t* buf, int q0, float v) {
-    float* st = reinterpret_cast<float*>(buf + C::OFF_STATS);
-    if (tid < C::BQ)
-      st[tid] = q0 + tid < N ? v * kLog2e : INFINITY;
-    else if (tid < 2 * C::BQ)
-      st[tid] = v;
+  // B operand of the bias k-step: bf16 ones at k = 0, 1, 2 (lanes of k-group
+  // 0), zeros elsewhere.
+  bf16x8 ones3;
+  {
+    const u32x4 w = {g ? 0u : 0x3F803F80u, g ? 0u : 0x00003F80u, 0u, 0u};
+    ones3 = as_bf16x8(w);
+    asm volatile("" : "+a"(ones3));
+  }
+  // A operand of the bias k-step for value x: (hi, mid, lo, 0, ..) with
+  // hi + mid + lo == x exactly (each part keeps the next 8 significand bits).
+  auto split3 = [](float x) {
+    const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;
+    const float r1 = x - __uint_as_float(hb);
+    const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(mb);
+    const u32x4 w = {(hb >> 16) | mb, __float_as_uint(r2) >> 16, 0u, 0u};
+    return as_bf16x8(w);
   };
-  tile_load<D, C::BQ, C::WAVES>(smem + C::OFF_Q, rq, 0, wave, lane);
-  tile_load<D, C::BQ, C::WAVES>(smem + C::OFF_DO, rdo, 0, wave, lane);
-  store_stat(smem, 0, load_stat(0));
+
+  // This lane's LDS byte offsets: row operands and statistics in the buffer
+  // the A phases read, transposing reads in the buffer the C phases read.
+  // Both start at buffer 0 and advance once per tile.
+  uint32_t ra[DK], rc[DB][2];
+#pragma unroll
+  for (int kk = 0; kk < DK; ++kk) ra[kk] = (uint32_t)(2 * row_read_off<D>(lane, kk));
+  uint32_t ra_st = (uint32_t)(2 * C::OFF_STATS + 4 * (lane & 31));
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) {
+    rc[cb][0] = (uint32_t)(2 * tr_read_off<D>(lane, cb, 0));
+    rc[cb][1] = (uint32_t)(2 * tr_read_off<D>(lane, cb, 1));
+  }
+  auto at = [&](uint32_t byte_off) {
+    return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(smem) + byte_off);
+  };
+
+  f32x16 s, dp;                  // S and dP of the latest A
+  u32x4 pw[2][2], sw[2][2];      // P and dS of two blocks as bf16 pairs: [set][16-query half]
+
+  // The first PF k-steps' operands of an A, and its query row's LSE and
+  // delta, are read ahead (a_pre) during the preceding B|C phase.
+  constexpr int PF = 2;
+  static_assert(PF <= RA, "prefetch within the read-ahead window");
+  bf16x8 pqa[PF], poa[PF];
+  float plse, pdel;
+  auto a_pre = [&](int qb) {
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) {
+      pqa[kk] = lds_bf16x8(at(ra[kk]) + qb * 32 * D + C::OFF_Q);
+      poa[kk] = lds_bf16x8(at(ra[kk]) + qb * 32 * D + C::OFF_DO);
+    }
+    // This lane's query row qb*32 + lane%32: its LSE and delta.
+    const float* st = reinterpret_cast<const float*>(at(ra_st)) + qb * 32;
+    plse = st[0];
+    pdel = st[C::BQ];
+  };
+
+  // A(block qb of the A buffer), after a_pre(qb), with loads m0 .. m0 + NIW
+  // - 1 of tile tl into buffer bl when do_dma.
+  auto a_phase = [&](int qb, bool do_dma, int bl, int tl, int m0) {
+    const uint16_t* rp[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) rp[kk] = at(ra[kk]) + qb * 32 * D;
+    const float lse_r = plse, del_r = pdel;
+    s = zero16();
+    dp = zero16();
+    bf16x8 qa[RA + 1], oa[RA + 1];
+#pragma unroll
+    for (int kk = 0; kk < RA; ++kk) {
+      if (kk < PF) {
+        qa[kk] = pqa[kk];
+        oa[kk] = poa[kk];
+      } else {
+        qa[kk] = lds_bf16x8(rp[kk] + C::OFF_Q);
+        oa[kk] = lds_bf16x8(rp[kk] + C::OFF_DO);
+      }
+    }
+    bf16x8 qbias, obias;
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) {
+      if (kk + RA < DK) {
+        qa[(kk + RA) % (RA + 1)] = lds_bf16x8(rp[kk + RA] + C::OFF_Q);
+        oa[(kk + RA) % (RA + 1)] = lds_bf16x8(rp[kk + RA] + C::OFF_DO);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s = mfma32(qa[kk % (RA + 1)], kreg[kk], s);
+      dp = mfma32(oa[kk % (RA + 1)], vreg[kk], dp);
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_dma && (kk & 1) == 0) dma(bl, tl, m0 + (kk >> 1));
+      if (kk == DK / 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        qbias = split3(lse_r * neg_inv_scale);
+        obias = split3(-del_r);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s = mfma32(qbias, ones3, s);
+    dp = mfma32(obias, ones3, dp);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // B of the latest A into P/dS set `bset`, interleaved with C(block cqb of
+  // the C buffer, P/dS set 1 - bset) when do_c.  Half-part hp
+  // covers score elements 4r + 2(hp&1) + {0,1}, r = hp/2; step n of C
+  // finishes half-parts n*HPS .. (multiply, pack) and starts those of step
+  // n+1 (scale, exp).  Three steps before the end, `pre` > 0 reads ahead for
+  // the next A: pre == 1 first publishes the next tile (wait for this wave's
+  // loads, barrier, move the A offsets on by `step`) and reads block 0 of
+  // it; pre == 2 reads block 1 of the current A buffer.
+  uint32_t step = 0;
+  auto bc_phase = [&](int bset, bool do_c, int cqb, int pre) {
+    float x[8][2];
+    auto stage1a = [&](int hp) {   // scale
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        x[hp][e] = s[4 * (hp >> 1) + 2 * (hp & 1) + e] * c2;
+        asm volatile("" : "+v"(x[hp][e]));
+      }
+    };
+    auto stage1b = [&](int hp) {   // exp
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        x[hp][e] = fast_exp2(x[hp][e]);
+        asm volatile("" : "+v"(x[hp][e]));
+      }
+    };
+    float y[8][2];
+    auto stage2a = [&](int hp) {   // dS = P dP'
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        y[hp][e] = x[hp][e] * dp[4 * (hp >> 1) + 2 * (hp & 1) + e];
+        asm volatile("" : "+v"(y[hp][e]));
+      }
+    };
+    auto stage2b = [&](int hp) {   // pack
+      const int r = hp >> 1;
+      uint32_t pv = pack_bf16x2(x[hp][0], x[hp][1]);
+      uint32_t sv = pack_bf16x2(y[hp][0], y[hp][1]);
+      asm volatile("" : "+v"(pv), "+v"(sv));
+      pw[bset][r >> 1][2 * (r & 1) + (hp & 1)] = pv;
+      sw[bset][r >> 1][2 * (r & 1) + (hp & 1)] = sv;
+    };
+
+    const uint16_t* tp[DB][2];
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tp[cb][h] = at(rc[cb][h]) + cqb * 32 * D;
+    bf16x8 oa[SA + 1], qa[SA + 1];
+    auto rd = [&](int n, bf16x8& o_, bf16x8& q_) {
+      const int h = n / DB, cb = n % DB;
+      o_ = tr_read2(tp[cb][0] + C::OFF_DO + h * 16 * D, tp[cb][1] + C::OFF_DO + h * 16 * D);
+      q_ = tr_read2(tp[cb][0] + C::OFF_Q + h * 16 * D, tp[cb][1] + C::OFF_Q + h * 16 * D);
+    };
+    if (do_c) {
+#pragma unroll
+      for (int n = 0; n < SA; ++n) rd(n, oa[n], qa[n]);
+    }
+#pragma unroll
+    for (int i = 0; i < HPS; ++i) stage1a(i);
+#pragma unroll
+    for (int i = 0; i < HPS; ++i) stage1b(i);
+    const int cset = 1 - bset;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      if (do_c && n + SA < NS) rd(n + SA, oa[(n + SA) % (SA + 1)], qa[(n + SA) % (SA + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int h = n / DB, cb = n % DB;
+      if (do_c) dvt[cb] = mfma32(oa[n % (SA + 1)], as_bf16x8(pw[cset][h]), dvt[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < HPS; ++i) {
+        if (n + 1 < NS) stage1a((n + 1) * HPS + i);
+        stage2a(n * HPS + i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_c) dkt[cb] = mfma32(qa[n % (SA + 1)], as_bf16x8(sw[cset][h]), dkt[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < HPS; ++i) {
+        if (n + 1 < NS) stage1b((n + 1) * HPS + i);
+        stage2b(n * HPS + i);
+      }
+      if (pre > 0 && n == NS - 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (pre == 1) {
+          wait_vmem();       // this wave's loads of the next tile have landed
+          __syncthreads();   // ... and everyone's; the tile before the current one is free
+#pragma unroll
+          for (int kk = 0; kk < DK; ++kk) ra[kk] += step;
+          ra_st += step;
+        }
+        a_pre(pre == 1 ? 0 : 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Prologue: tile 0 published in buffer 0, tile 1 in flight to buffer 1,
+  // A(0), B(0), A(1) done.
+#pragma unroll
+  for (int m = 0; m < 2 * NIW; ++m) dma(0, 0, m);
   wait_vmem();
   __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 2 * NIW; ++m) dma(1, 1, m);
+  a_pre(0);
+  a_phase(0, false, 0, 0, 0);
+  bc_phase(0, false, 0, 2);
+  a_phase(1, false, 0, 0, 0);
 
-  for (int it = 0; it < nqt; ++it) {
-    const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
-    const uint16_t* Qs = buf + C::OFF_Q;
-    const uint16_t* dOs = buf + C::OFF_DO;
-    const float* lse2s = reinterpret_cast<const float*>(buf + C::OFF_STATS);
-    const float* dls = lse2s + C::BQ;
-    const bool more = it + 1 < nqt;
-    uint16_t* nbuf = smem + ((it + 1) & 1) * C::BUF_ELEMS;
-    float stat = 0.0f;
-    if (more) {
-      tile_load<D, C::BQ, C::WAVES>(nbuf + C::OFF_Q, rq, (it + 1) * C::BQ, wave, lane);
-      tile_load<D, C::BQ, C::WAVES>(nbuf + C::OFF_DO, rdo, (it + 1) * C::BQ, wave, lane);
-      stat = load_stat((it + 1) * C::BQ);
+  int b0 = 0, b1 = 1, b2 = 2;   // buffers of tiles t, t+1, t+2
+  for (int t = 0; t < nqt; ++t) {
+    step = (uint32_t)((b1 - b0) * C::BUF_ELEMS * 2);   // next buffer, mod 2^32
+    bc_phase(1, true, 0, 1);                   // B(2t+1) | C(2t); publishes tile t+1
+    a_phase(0, true, b2, t + 2, 0);            // A(2t+2), first half of tile t+2's loads
+    bc_phase(0, true, 1, 2);                   // B(2t+2) | C(2t+1)
+    a_phase(1, true, b2, t + 2, NIW);          // A(2t+3), second half
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {          // C phases move on to tile t+1
+      rc[cb][0] += step;
+      rc[cb][1] += step;
     }
-
-    // One 32-query block at a time: S = Q K^T and dP = dO V^T (operands
-    // read kReadAhead k-steps ahead), then P and dS, then dV^T += dO^T P and
-    // dK^T += Q^T dS for the block's two 16-query steps (dO^T and Q^T
-    // gathered with transposing reads kStepAhead steps ahead).
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
-      {
-        constexpr int RA = kReadAhead;
-        bf16x8 qa[RA + 1], oa[RA + 1];
-#pragma unroll
-        for (int kk = 0; kk < RA; ++kk) {
-          qa[kk] = row_operand<D>(Qs, qb * 32 + li, 2 * kk + g);
-          oa[kk] = row_operand<D>(dOs, qb * 32 + li, 2 * kk + g);
-        }
-#pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) {
-          if (kk + RA < C::DK) {
-            qa[(kk + RA) % (RA + 1)] = row_operand<D>(Qs, qb * 32 + li, 2 * (kk + RA) + g);
-            oa[(kk + RA) % (RA + 1)] = row_operand<D>(dOs, qb * 32 + li, 2 * (kk + RA) + g);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          s = mfma32(qa[kk % (RA + 1)], kreg[kk], s);
-          dp = mfma32(oa[kk % (RA + 1)], vreg[kk], dp);
-        }
-      }
-      // P and dS; element 4r + e is query qb*32 + 8r + 4g + e.
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 pw, sw;
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int r = 2 * h + rr;
-          const int qo = qb * 32 + 8 * r + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qo);
-          float p[4], d[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = fast_exp2(fmaf(s[4 * r + e], c2, -l4[e]));
-            d[e] = p[e] * (dp[4 * r + e] - d4[e]);
-          }
-          pw[2 * rr] = pack_bf16x2(p[0], p[1]);
-          pw[2 * rr + 1] = pack_bf16x2(p[2], p[3]);
-          sw[2 * rr] = pack_bf16x2(d[0], d[1]);
-          sw[2 * rr + 1] = pack_bf16x2(d[2], d[3]);
-        }
-        pb[h] = as_bf16x8(pw);
-        sb[h] = as_bf16x8(sw);
-      }
-      {
-        constexpr int SA = kStepAhead, NS = 2 * C::DB;   // steps n = (h, cb)
-        bf16x8 oa[SA + 1], qa[SA + 1];
-#pragma unroll
-        for (int n = 0; n < SA; ++n) {
-          oa[n] = tr_operand<D>(dOs, (2 * qb + n / C::DB) * 16, (n % C::DB) * 32, lane);
-          qa[n] = tr_operand<D>(Qs, (2 * qb + n / C::DB) * 16, (n % C::DB) * 32, lane);
-        }
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          if (n + SA < NS) {
-            const int m = n + SA;
-            oa[m % (SA + 1)] = tr_operand<D>(dOs, (2 * qb + m / C::DB) * 16, (m % C::DB) * 32, lane);
-            qa[m % (SA + 1)] = tr_operand<D>(Qs, (2 * qb + m / C::DB) * 16, (m % C::DB) * 32, lane);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          const int h = n / C::DB, cb = n % C::DB;
-          dvt[cb] = mfma32(oa[n % (SA + 1)], pb[h], dvt[cb]);
-          dkt[cb] = mfma32(qa[n % (SA + 1)], sb[h], dkt[cb]);
-        }
-      }
-    }
-
-    if (more) store_stat(nbuf, (it + 1) * C::BQ, stat);
-    wait_vmem();      // this wave's loads of the next tile have landed
-    __syncthreads();  // ... and everyone's; the current tile is no longer read
+    b0 = b1;
+    b1 = b2;
+    b2 = b2 == 2 ? 0 : b2 + 1;
   }
+  wait_vmem();   // no direct loads left in flight at exit
 
   // dV^T / dK^T element i of block cb: column cb*32 + 8*(i/4) + 4g + i%4 of
   // this lane's key row.
@@ -249,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* dkr = dk + hoff + (int64_t)key * D;
     uint16_t* dvr = dv + hoff + (int64_t)key * D;
 #pragma unroll
-    for (int cb = 0; cb < C::DB; ++cb)
+    for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = cb * 32 + 8 * r + 4 * g;

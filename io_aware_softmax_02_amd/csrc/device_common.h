@@ -41,6 +41,15 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Four 4-vectors as one accumulator tuple (a in elements 0..3, ...).
+__device__ __forceinline__ f32x16 cat16(const f32x4& a, const f32x4& b, const f32x4& c,
+                                        const f32x4& d) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  const f32x8 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return __builtin_bit_cast(bf16x8, z);

@@ -74,6 +74,20 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t lds,
       : "memory");
 }
 
+// The same with 4 bytes per lane: lane L's dword lands at lds + 4 L.
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t lds,
+                                         uint32_t soff = 0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dword %1, %2, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(lds), "s"(soff)
+      : "memory");
+}
+
 // Copies rows [r0, r0 + R) of one head of a [N][D] bf16 matrix into a tile.
 // The R*D/8 chunks go out as 64-chunk wave instructions; wave w of NW issues
 // instructions w, w + NW, ...  Rows at or past the end of `src` read as 0.
@@ -113,6 +127,62 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int rb, int c
   const int r1 = rb + 4 * g + a, r2 = r1 + 8;
   const uint16_t* p1 = tile + tile_off<D>(r1, col >> 3) + (col & 7);
   const uint16_t* p2 = tile + tile_off<D>(r2, col >> 3) + (col & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p1));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p2));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
+  return as_bf16x8(w);
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled tiles with per-lane offset tables.  When a tile is loaded one
+// instruction at a time (interleaved with other work) and read through
+// per-lane pointers computed once, neither side does address arithmetic in
+// the loop.
+//
+// Direct loads: wave w of NW issues instructions u = 0, 1, ... covering
+// physical chunks (w + u NW) * 64 + lane.  Consecutive instructions of a wave
+// are NW*64/(D/8) rows apart, a multiple of the swizzle period (16 rows), so
+// the per-lane source offset is the same for every u (tile_dma_voff) and the
+// rest of the address is wave-uniform.
+template <int D, int NW>
+__device__ __forceinline__ uint32_t tile_dma_voff(int wave, int lane) {
+  constexpr int NC = D / 8;
+  const int lin = wave * 64 + lane, row = lin / NC, phys = lin % NC;
+  return (uint32_t)((row * D + ((phys ^ swz<D>(row)) << 3)) * 2);
+}
+// Instruction u of this wave: `tile_lds` is the tile's LDS byte address and
+// `row0_bytes` the byte offset of the tile's first row in `src` (both
+// wave-uniform).
+template <int D, int NW>
+__device__ __forceinline__ void tile_dma(uint32_t tile_lds, rsrc_t src, uint32_t voff,
+                                         uint32_t row0_bytes, int wave, int u) {
+  constexpr int RSTEP = NW * 64 / (D / 8);
+  static_assert(RSTEP % 16 == 0, "whole swizzle periods between instructions");
+  lds_dma16(src, voff, tile_lds + (uint32_t)((wave + u * NW) * 1024),
+            row0_bytes + (uint32_t)(u * RSTEP * D * 2));
+}
+// Element offset of this lane's row operand at k-step kk in rows 0..31 (row
+// lane % 32, logical chunk 2 kk + lane / 32).  32-row block kb adds kb*32*D.
+template <int D>
+__device__ __forceinline__ int row_read_off(int lane, int kk) {
+  const int r = lane & 31, c = 2 * kk + (lane >> 5);
+  return r * D + ((c ^ swz<D>(r)) << 3);
+}
+// Element offset of this lane's half-h transposing read (see tr_operand) of
+// 32-column block cb in rows 0..15.  16-row step t adds t*16*D.
+template <int D>
+__device__ __forceinline__ int tr_read_off(int lane, int cb, int h) {
+  const int i16 = lane & 15, q = lane >> 4;
+  const int a = i16 >> 2, b = i16 & 3, g = q >> 1;
+  const int col = cb * 32 + 16 * (q & 1) + 4 * b;
+  const int r = 4 * g + a + 8 * h;
+  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+}
+// The transposed operand from the two halves' addresses.
+__device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p2) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p1));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
