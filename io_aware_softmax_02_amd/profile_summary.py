@@ -1,0 +1,139 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+Not used by the library itself; it turns the raw files a profiling run
+leaves in its output directory into the short text summaries that are kept:
+
+  python -m io_aware_softmax_02_amd.profile_summary trace  DB_GLOB TITLE COMMAND
+      kernel-trace statistics (a --kernel-trace --stats database) as markdown
+  python -m io_aware_softmax_02_amd.profile_summary counters CSV TITLE COMMAND
+      per-dispatch averages of every counter in a --pmc CSV as markdown
+  python -m io_aware_softmax_02_amd.profile_summary traffic FETCH_CSV WRITE_CSV OUT_JSON
+      HBM bytes per launch from FETCH_SIZE / WRITE_SIZE passes, calibrated
+      against a 512 MiB device copy made in the same process (bench.py makes
+      one before its timed region); bench.py reads OUT_JSON
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 512 << 20
+KERNELS = {"fwd_bf16_kernel": "fwd_bf16", "bwd_dkdv_kernel": "bwd_dkdv_bf16",
+           "bwd_dq_kernel": "bwd_dq_bf16", "bwd_pre_kernel": "bwd_pre_bf16",
+           "merge_kernel": "merge_bf16"}
+# Sources whose digest a traffic record carries: a record is only reported
+# while the kernels it measured are unchanged.
+TRAFFIC_SOURCES = ["io_aware_softmax_02_amd/csrc/" + x for x in
+                   ("attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "lds_tile.h", "device_common.h")] + \
+                  ["io_aware_softmax_02_amd/build.py"]
+
+
+def short(name: str) -> str:
+    return re.sub(r"\(.*", "", name.replace("void ", "").replace("fa::(anonymous namespace)::", ""))
+
+
+def source_digests() -> dict:
+    return {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
+            for p in TRAFFIC_SOURCES}
+
+
+def trace(db_glob: str, title: str, cmd: str) -> str:
+    con = sqlite3.connect(glob.glob(db_glob)[0])
+    rows = con.execute("select name, total_calls, total_duration, average, percentage "
+                       "from top_kernels").fetchall()
+    res = {r[0]: r for r in con.execute(
+        "select name, lds_size, vgpr_count, accum_vgpr_count, sgpr_count, grid_x, workgroup_x "
+        "from kernels group by name").fetchall()}
+    out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n",
+           f"```\n{cmd}\n```\n",
+           "| kernel | calls | total µs | average µs | % | grid (threads) | block | LDS B | arch VGPR | acc VGPR |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for n, calls, tot, avg, pct in rows:
+        r = res.get(n)
+        out.append(f"| `{short(n)}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.1f} | "
+                   f"{r[5]} | {r[6]} | {r[1]} | {r[2]} | {r[3]} |")
+    return "\n".join(out) + "\n"
+
+
+def per_dispatch(path: str) -> dict:
+    """{kernel: {counter: mean over dispatches of the per-dispatch sum}}"""
+    agg = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for r in csv.DictReader(open(path)):
+        agg[short(r["Kernel_Name"])][r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: {c: sum(d.values()) / len(d) for c, d in cs.items()} for k, cs in agg.items()}
+
+
+def counters(path: str, title: str, cmd: str) -> str:
+    data = per_dispatch(path)
+    names = sorted({c for cs in data.values() for c in cs})
+    out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n",
+           f"```\n{cmd}\n```\n",
+           "Per-dispatch values, averaged over the profiled dispatches (summed over all XCDs, "
+           "shader engines and SIMDs as rocprofv3 reports them).\n",
+           "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k, cs in sorted(data.items()):
+        out.append(f"| `{k}` | " + " | ".join(f"{cs.get(c, 0):,.0f}" for c in names) + " |")
+    return "\n".join(out) + "\n"
+
+
+def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
+    f = {k: v["FETCH_SIZE"] for k, v in per_dispatch(fetch_csv).items() if "FETCH_SIZE" in v}
+    w = {k: v["WRITE_SIZE"] for k, v in per_dispatch(write_csv).items() if "WRITE_SIZE" in v}
+    copy = next(k for k in f if "copyBuffer" in k)
+    rf = COPY_BYTES / (f[copy] * 1024.0)
+    wf = COPY_BYTES / (w[copy] * 1024.0)
+    sha = source_digests()
+    kern = {}
+    for k in f:
+        for pref, name in KERNELS.items():
+            if k.startswith(pref) and "128" in k:
+                kern[name] = {"rocprof_name": k, "fetch_size_kib": f[k], "write_size_kib": w.get(k),
+                              "read_bytes": f[k] * 1024 * rf, "write_bytes": w.get(k, 0) * 1024 * wf,
+                              "source_sha256": sha}
+    rx = "|".join(list(KERNELS) + ["copyBuffer"])
+    doc = {"what": "HBM traffic per launch at B=1 H=16 N=8192 d=128, from rocprofv3 FETCH_SIZE "
+                   "and WRITE_SIZE (KiB per dispatch), each scaled by the same counter on a "
+                   "512 MiB device copy run in the same bench process",
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": f[copy],
+                           "write_size_kib": w[copy], "read_factor": rf, "write_factor": wf},
+           "commands": [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} --kernel-include-regex '{rx}' "
+                        f"-f csv -d gpurun_out/pmc_{t} -o pmc -- python3 bench.py --steps 2 "
+                        f"--warmup 1 --no-cpu-baseline" for c, t in (("FETCH_SIZE", "F"), ("WRITE_SIZE", "W"))]
+                       + ["python -m io_aware_softmax_02_amd.profile_summary traffic "
+                          "gpurun_out/pmc_F/pmc_counter_collection.csv "
+                          "gpurun_out/pmc_W/pmc_counter_collection.csv " + out_json],
+           "kernels": kern}
+    with open(out_json, "w") as fh:
+        json.dump(doc, fh, indent=1)
+    return doc
+
+
+def main(argv: list[str]) -> int:
+    if len(argv) < 2:
+        print(__doc__)
+        return 2
+    cmd = argv[1]
+    if cmd == "trace":
+        sys.stdout.write(trace(argv[2], argv[3], argv[4]))
+    elif cmd == "counters":
+        sys.stdout.write(counters(argv[2], argv[3], argv[4]))
+    elif cmd == "traffic":
+        doc = traffic(argv[2], argv[3], argv[4])
+        for k, v in doc["kernels"].items():
+            print(k, round(v["read_bytes"] / 1e6, 1), "MB read", round(v["write_bytes"] / 1e6, 1), "MB written")
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))
