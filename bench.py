@@ -12,6 +12,12 @@ HIP events on the stream it runs on) and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Two further measurements print one JSON line per case instead:
+    python bench.py --sweep     forward and fwd+bwd over N = 2048 .. 131072
+                                 (d = 128, H = 16), with peak device memory
+    python bench.py --splitkv   split-KV forward + merge against the plain
+                                 forward when B*H is small
 """
 
 from __future__ import annotations
@@ -45,6 +51,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle runs (forward+backward)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sequence-length sweep instead of the headline measurement")
+    ap.add_argument("--splitkv", action="store_true",
+                    help="split-KV forward + merge measurement instead of the headline one")
     return ap.parse_args()
 
 
@@ -59,6 +69,12 @@ def time_launches(fn, n, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n
+
+
+def median_time(fn, inner, stream, outer=5):
+    """Median over `outer` runs of the average duration (ms) of `inner`
+    back-to-back launches of fn (so launch gaps do not count)."""
+    return sorted(time_launches(fn, inner, stream) for _ in range(outer))[outer // 2]
 
 
 def measured_traffic(kernel):
@@ -106,6 +122,101 @@ def cpu_baseline(w, heads):
                       f"forward+backward, float64 numpy, {dt:.1f} s"}
 
 
+def sweep(args):
+    """Forward and fwd+bwd throughput and peak device memory over N at d=128,
+    H=16, B=1 (the pages' long-context sizes, 2k .. 128k).  Alongside each
+    line: the bytes one fp32 score matrix per head would take (the quantity
+    the tiled method never stores)."""
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    B, H, d = 1, 16, 128
+    for N in (2048, 4096, 8192, 16384, 32768, 65536, 131072):
+        q, k, v, dO = (x.to(dev) for x in synth.make_qkv(B, H, N, d, torch.bfloat16, seed=N,
+                                                        backward=True))
+        s = synth.default_scale(d)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        fa.fa_fwd(q, k, v, s, o=o, lse=lse)
+        torch.cuda.synchronize()
+        peak_fwd = torch.cuda.max_memory_allocated() - base
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        inner = max(1, min(20, int(2e4 / (N / 1024) ** 2)))
+        outer = 5 if N <= 32768 else 3
+        fwd = lambda: fa.fa_fwd(q, k, v, s, o=o, lse=lse)
+        bwd = lambda: fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+        fwd(); bwd()
+        torch.cuda.synchronize()
+        med_f = median_time(fwd, inner, stream, outer)
+        med_b = median_time(bwd, inner, stream, outer)
+        fl_f = 4.0 * B * H * N * N * d
+        print(json.dumps({
+            "sweep": "N", "B": B, "H": H, "N": N, "d": d, "launches": inner, "runs": outer,
+            "ms_fwd": round(med_f, 4), "ms_bwd": round(med_b, 4),
+            "fwd_tflops": round(fl_f / (med_f * 1e-3) / 1e12, 1),
+            "fwdbwd_tflops": round(3.5 * fl_f / ((med_f + med_b) * 1e-3) / 1e12, 1),
+            "fwd_peak_extra_bytes": int(peak_fwd),
+            "inputs_outputs_bytes_fwd": int(4 * q.numel() * 2 + lse.numel() * 4),
+            "fp32_scores_per_head_bytes": int(N * N * 4),
+        }), flush=True)
+        del q, k, v, dO, o, lse, dq, dk, dv, ws
+
+
+def splitkv(args):
+    """Split-KV forward + merge against the plain forward at small B*H,
+    where the plain forward has fewer workgroups than the chip has CUs.
+    The merge kernel's roofline is HBM bandwidth: per row it reads
+    n_split * (4d + 4) bytes and writes 2d + 4."""
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    d = 128
+    for B, H, N in ((1, 1, 8192), (1, 2, 16384), (1, 1, 65536), (1, 16, 8192)):
+        q, k, v, _ = (x.to(dev) if x is not None else None
+                      for x in synth.make_qkv(B, H, N, d, torch.bfloat16, seed=7))
+        s = synth.default_scale(d)
+        fl = 4.0 * B * H * N * N * d
+        o0 = torch.empty_like(q)
+        l0 = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        fwd = lambda: fa.fa_fwd(q, k, v, s, o=o0, lse=l0)
+        fwd()
+        torch.cuda.synchronize()
+        ms_plain = median_time(fwd, 10, stream)
+        res = {"splitkv": True, "B": B, "H": H, "N": N, "d": d,
+               "plain_ms": round(ms_plain, 4), "plain_tflops": round(fl / (ms_plain * 1e-3) / 1e12, 1),
+               "splits": []}
+        for P in (2, 4, 8, 16, 32):
+            if P > fa.fa_fwd_split_max(B, H, N, d):
+                continue
+            op, lp = fa.fa_fwd_split(q, k, v, P, s)
+            o, lse = fa.fa_merge(op, lp)
+            split = lambda: fa.fa_fwd_split(q, k, v, P, s, o_part=op, lse_part=lp)
+            merge = lambda: fa.fa_merge(op, lp, o=o, lse=lse)
+            torch.cuda.synchronize()
+            ms_s = median_time(split, 10, stream)
+            ms_m = median_time(merge, 10, stream)
+            rows = B * H * N
+            mbytes = P * rows * (4 * d + 4) + rows * (2 * d + 4)
+            res["splits"].append({
+                "n_split": P, "split_ms": round(ms_s, 4), "merge_ms": round(ms_m, 4),
+                "total_tflops": round(fl / ((ms_s + ms_m) * 1e-3) / 1e12, 1),
+                "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
+                "merge_frac_of_hbm": round(mbytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+            del op, lp, o, lse
+        print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +224,10 @@ def main():
               "single MI355X (heads shard across GPUs with no communication, which is not "
               "built here). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep(args)
+    if args.splitkv:
+        return splitkv(args)
 
     import torch
     import io_aware_softmax_02_amd as fa
@@ -170,6 +285,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
     peak_mem = torch.cuda.max_memory_allocated()
+    # Per-step spread (after the timed region): median and minimum of single steps.
+    per_step = sorted(time_launches(step, 1, stream) for _ in range(max(args.steps, 5)))
 
     # Per-kernel launch times (each entry point launches one kernel except
     # fa_bwd, whose three stages are timed through their own entry points).
@@ -209,6 +326,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

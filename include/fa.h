@@ -78,6 +78,41 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                  fa_stream_t stream);
 
+/* Split-KV forward (more workgroups when B*H is small; also the per-device
+ * step of a key-sharded forward).  The keys are cut into n_split contiguous
+ * ranges of whole key tiles (128 keys at d = 128, 64 at d = 64): range p
+ * holds tiles [p*T/n_split, (p+1)*T/n_split) with T = ceil(N/tile) and
+ * integer division, so every range holds at least one tile.  For each range
+ * and query row i it writes
+ *   lse_part[p][b][h][i]    = ln sum_{j in range p} exp(scale * q_i . k_j)
+ *   o_part[p][b][h][i][:]   = sum_{j in range p} exp(scale * q_i . k_j - lse_part) v_j
+ * i.e. the forward restricted to the range (fp32 output, normalised by the
+ * range's own sum).  o_part is float32 [n_split][B][H][N][d] and lse_part
+ * float32 [n_split][B][H][N], both 16-byte aligned.  1 <= n_split <=
+ * fa_fwd_split_max(B,H,N,d), else FA_ERR_SHAPE.  Tiling per range as in
+ * fa_fwd; the ranges are recombined by fa_merge (star-observatory fable
+ * page, section "兩大核心魔法"). */
+int64_t fa_fwd_split_max(int64_t B, int64_t H, int64_t N, int64_t d); /* -1: invalid shape */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part,
+                       float* lse_part, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       int64_t n_split, fa_stream_t stream);
+
+/* Merge of n_split partial results (any source: fa_fwd_split, other
+ * devices, ...).  For each row, with m = max_p lse_part[p]:
+ *   lse = m + ln sum_p exp(lse_part[p] - m)
+ *   o   = sum_p exp(lse_part[p] - lse) * o_part[p]          (bf16 output, RNE)
+ * the rescale identity of the star-observatory fable page (section
+ * "兩大核心魔法"); the order of the parts does not matter (算珠楼的掌簿人,
+ * section 四).  A part with lse_part = -inf contributes nothing (its o_part
+ * values are read but not used, so they may be NaN); a row whose parts are
+ * all -inf gets o = 0, lse = -inf.
+ * o_part float32 [n_split][B][H][N][d], lse_part float32 [n_split][B][H][N]
+ * (inputs); o bf16 [B][H][N][d], lse float32 [B][H][N] (outputs).  d must be
+ * 64 or 128; n_split >= 1; 16-byte alignment; outputs may not overlap the
+ * inputs (FA_ERR_ALIAS). */
+fa_status fa_merge(const float* o_part, const float* lse_part, int64_t n_split, void* o,
+                   float* lse, int64_t B, int64_t H, int64_t N, int64_t d, fa_stream_t stream);
+
 /* Bytes of workspace fa_bwd needs: one fp32 per query row (D = rowsum(dO*O)),
  * rounded up to 256.  0 for an empty problem.  (size_t)-1 for invalid sizes. */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);

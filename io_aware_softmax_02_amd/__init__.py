@@ -21,7 +21,7 @@ import torch
 from ._lib import LIB, FAError, FA_OK, status_str  # noqa: F401
 
 __all__ = [
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
+    "fa_fwd", "fa_fwd_split_max", "fa_fwd_split", "fa_merge", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
     "fa_bwd_dq", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
     "default_scale", "FAError", "status_str",
 ]
@@ -98,6 +98,68 @@ def fa_fwd(q, k, v, scale: Optional[float] = None, o=None, lse=None, stream=None
            ) -> Tuple[torch.Tensor, torch.Tensor]:
     """bf16 forward.  Returns (o, lse); o bf16 [B,H,N,d], lse fp32 [B,H,N]."""
     return _fwd(LIB.fa_fwd, "fa_fwd", torch.bfloat16, q, k, v, scale, o, lse, stream)
+
+
+def fa_fwd_split_max(B: int, H: int, N: int, d: int) -> int:
+    """Largest key-range count fa_fwd_split accepts (-1 for an invalid shape)."""
+    return int(LIB.fa_fwd_split_max(B, H, N, d))
+
+
+def fa_fwd_split(q, k, v, n_split: int, scale: Optional[float] = None, o_part=None,
+                 lse_part=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV forward.  Returns (o_part fp32 [n_split,B,H,N,d], lse_part fp32
+    [n_split,B,H,N]): each key range's own normalised output and LSE."""
+    shape = _shape4(q, "q", torch.bfloat16)
+    _same(shape, k, "k", torch.bfloat16)
+    _same(shape, v, "v", torch.bfloat16)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    n = int(n_split)
+    if o_part is None:
+        o_part = torch.empty((max(n, 0), B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((max(n, 0), B, H, N), dtype=torch.float32, device=q.device)
+    _parts(o_part, lse_part, n, shape)
+    with torch.cuda.device(q.device):
+        _check(LIB.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
+                                B, H, N, d, float(scale), n, _stream(q.device, stream)),
+               "fa_fwd_split")
+    return o_part, lse_part
+
+
+def fa_merge(o_part, lse_part, o=None, lse=None, stream=None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge of partial results.  o_part fp32 [P,B,H,N,d], lse_part fp32
+    [P,B,H,N]; returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    if not isinstance(o_part, torch.Tensor) or o_part.dim() != 5:
+        raise ValueError("o_part must be a [P, B, H, N, d] tensor")
+    n = int(o_part.shape[0])
+    shape = tuple(o_part.shape[1:])
+    _parts(o_part, lse_part, n, shape)
+    B, H, N, d = shape
+    if o is None:
+        o = torch.empty(shape, dtype=torch.bfloat16, device=o_part.device)
+    else:
+        _same(shape, o, "o", torch.bfloat16)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    else:
+        _rows(lse, "lse", shape)
+    with torch.cuda.device(o_part.device):
+        _check(LIB.fa_merge(_ptr(o_part), _ptr(lse_part), n, _ptr(o), _ptr(lse), B, H, N, d,
+                            _stream(o_part.device, stream)), "fa_merge")
+    return o, lse
+
+
+def _parts(o_part, lse_part, n: int, shape) -> None:
+    for x, name, tail in ((o_part, "o_part", tuple(shape)), (lse_part, "lse_part", tuple(shape[:3]))):
+        if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if x.dtype != torch.float32 or not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32")
+        if tuple(x.shape) != (max(n, 0),) + tail:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {(n,) + tail}")
 
 
 def fa_fwd_f32(q, k, v, scale: Optional[float] = None, o=None, lse=None, stream=None

@@ -22,6 +22,9 @@ _st = ctypes.c_int
 PROTOTYPES = {
     "fa_status_str": (ctypes.c_char_p, [_st]),
     "fa_fwd": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
+    "fa_fwd_split_max": (_i64, [_i64, _i64, _i64, _i64]),
+    "fa_fwd_split": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _i64, _p]),
+    "fa_merge": (_st, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "fa_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fa_bwd": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
                      _i64, _i64, _i64, _i64, _f, _p]),

@@ -16,6 +16,12 @@ int launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const floa
 int launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const float* lse,
                        const void* dO, const float* delta, void* dq, int64_t BH, int64_t N,
                        int64_t d, float scale, hipStream_t stream);
+int fwd_split_tile(int64_t d);
+int launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* o_part,
+                          float* lse_part, int64_t BH, int64_t N, int64_t d, float scale,
+                          int nsplit, hipStream_t stream);
+int launch_merge_bf16(const float* o_part, const float* lse_part, int nsplit, int64_t rows,
+                      int64_t d, void* o, float* lse, hipStream_t stream);
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
 int launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
@@ -95,6 +101,45 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   FA_TRY(check_fwd(q, k, v, o, lse, s, scale, true));
   if (s.empty()) return FA_OK;
   return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
+}
+
+int64_t fa_fwd_split_max(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const Shape s{B, H, N, d};
+  if (fa::check_shape(s, true) != FA_OK) return -1;
+  return fa::split_max(s, fa::fwd_split_tile(d));
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part,
+                       float* lse_part, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       int64_t n_split, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  FA_TRY(fa::check_scale(scale));
+  FA_TRY(fa::check_parts(s, n_split));
+  if (s.empty()) return FA_OK;
+  if (n_split > fa::split_max(s, fa::fwd_split_tile(d))) return FA_ERR_SHAPE;
+  FA_TRY(fa::check_ptrs({q, k, v, o_part, lse_part}, 16));
+  const Sizes z = sizes(s, 2);
+  const size_t np = static_cast<size_t>(n_split);
+  FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}},
+                         {{o_part, np * z.tensor * 2}, {lse_part, np * z.rows}}));
+  return from_hip(fa::launch_fwd_split_bf16(q, k, v, o_part, lse_part, B * H, N, d, scale,
+                                            static_cast<int>(n_split), as_stream(stream)));
+}
+
+fa_status fa_merge(const float* o_part, const float* lse_part, int64_t n_split, void* o,
+                   float* lse, int64_t B, int64_t H, int64_t N, int64_t d, fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  FA_TRY(fa::check_parts(s, n_split));
+  if (s.empty()) return FA_OK;
+  FA_TRY(fa::check_ptrs({o_part, lse_part, o, lse}, 16));
+  const Sizes z = sizes(s, 2);
+  const size_t np = static_cast<size_t>(n_split);
+  FA_TRY(fa::check_alias({{o_part, np * z.tensor * 2}, {lse_part, np * z.rows}},
+                         {{o, z.tensor}, {lse, z.rows}}));
+  return from_hip(fa::launch_merge_bf16(o_part, lse_part, static_cast<int>(n_split), s.rows(),
+                                        d, o, lse, as_stream(stream)));
 }
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {

@@ -29,6 +29,11 @@
 //   a base register plus an immediate offset.
 //   Base-2 domain: c = scale * log2(e); p = 2^(c s - m) with m in log2 units;
 //   LSE = ln 2 * (m + log2 l).
+//
+// Split-KV mode (SPLIT): the key tiles are cut into nsplit contiguous ranges
+// and each workgroup handles one range of one query tile, writing that
+// range's own normalised output (fp32) and LSE.  The ranges are recombined
+// by the merge kernel (attn_merge.hip) with the same rescale identity.
 #include "lds_tile.h"
 
 namespace fa {
@@ -65,16 +70,19 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return x * base + (x < rem ? x : rem) + idx;
 }
 
-template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4>
+template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int N,
-    int ntq, float c2) {
+    const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N,
+    int ntq, float c2, int nsplit, int64_t part_rows) {
   using C = FwdCfg<D, QB, BC, NWAVES>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
+  // Logical id = ((bh * nsplit) + p) * ntq + qt: the query tiles of one
+  // (head, key range) are consecutive and share an XCD.
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / ntq, qt = logical - bh * ntq;
+  const int qt = logical % ntq, hp = logical / ntq;
+  const int bh = SPLIT ? hp / nsplit : hp, part = SPLIT ? hp - bh * nsplit : 0;
   const int64_t hoff = (int64_t)bh * N * D;
   const uint32_t hbytes = (uint32_t)N * D * 2;
   const rsrc_t rq = make_rsrc(q + hoff, hbytes);
@@ -109,17 +117,22 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     l_run[qb] = 0.0f;
   }
 
+  // Key tiles [j0, j1): all of them, or this workgroup's range in split mode
+  // (whole tiles, as even as possible; every range holds at least one tile).
   const int nkt = (N + BC - 1) / BC;
-  rowop_load<D, BC, C::WAVES>(smem, rk, 0, wave, lane);
-  trop_load<D, BC, C::WAVES>(smem + C::TILE, rv, 0, wave, lane);
+  const int j0 = SPLIT ? (int)((int64_t)part * nkt / nsplit) : 0;
+  const int j1 = SPLIT ? (int)((int64_t)(part + 1) * nkt / nsplit) : nkt;
+  rowop_load<D, BC, C::WAVES>(smem, rk, j0 * BC, wave, lane);
+  trop_load<D, BC, C::WAVES>(smem + C::TILE, rv, j0 * BC, wave, lane);
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const uint16_t* kl = smem + (j & 1) * C::BUF_ELEMS + 8 * lane;   // this lane's K reads
-    const uint16_t* vl = smem + (j & 1) * C::BUF_ELEMS + C::TILE + 4 * lane;
-    if (j + 1 < nkt) {
-      uint16_t* nb = smem + ((j + 1) & 1) * C::BUF_ELEMS;
+  for (int j = j0; j < j1; ++j) {
+    const int jb = (j - j0) & 1;   // buffer of tile j
+    const uint16_t* kl = smem + jb * C::BUF_ELEMS + 8 * lane;   // this lane's K reads
+    const uint16_t* vl = smem + jb * C::BUF_ELEMS + C::TILE + 4 * lane;
+    if (j + 1 < j1) {
+      uint16_t* nb = smem + (jb ^ 1) * C::BUF_ELEMS;
       rowop_load<D, BC, C::WAVES>(nb, rk, (j + 1) * BC, wave, lane);
       trop_load<D, BC, C::WAVES>(nb + C::TILE, rv, (j + 1) * BC, wave, lane);
     }
@@ -252,33 +265,48 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     const float l_tot = sum_across_halves(l_run[qb]);
     if (qrow < N) {
       const float inv = 1.0f / l_tot;
-      uint16_t* orow = o + hoff + (int64_t)qrow * D;
+      if (SPLIT) {   // fp32 output of this key range, at part p of the partial tensors
+        float* orow = static_cast<float*>(o) + part * part_rows * D + hoff + (int64_t)qrow * D;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[qb][db][4 * r + 0] * inv, acc[qb][db][4 * r + 1] * inv);
-          w[1] = pack_bf16x2(acc[qb][db][4 * r + 2] * inv, acc[qb][db][4 * r + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * g) = w;
-        }
-      if (g == 0) lse[(int64_t)bh * N + qrow] = kLn2 * (m_run[qb] + log2f(l_tot));
+          for (int r = 0; r < 4; ++r) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = acc[qb][db][4 * r + e] * inv;
+            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * r + 4 * g) = w;
+          }
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(o) + hoff + (int64_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[qb][db][4 * r + 0] * inv, acc[qb][db][4 * r + 1] * inv);
+            w[1] = pack_bf16x2(acc[qb][db][4 * r + 2] * inv, acc[qb][db][4 * r + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * g) = w;
+          }
+      }
+      if (g == 0)
+        lse[(SPLIT ? part * part_rows : 0) + (int64_t)bh * N + qrow] =
+            kLn2 * (m_run[qb] + log2f(l_tot));
     }
   }
 }
 
-template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4>
-int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-           int64_t BH, int64_t N, float scale, hipStream_t stream) {
+template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4, bool SPLIT = false>
+int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
+           int64_t BH, int64_t N, float scale, int nsplit, hipStream_t stream) {
   using C = FwdCfg<D, QB, BC, NWAVES>;
   const int ntq = (int)((N + C::BR - 1) / C::BR);
-  const int64_t nwg = (int64_t)ntq * BH;
-  auto kern = fwd_bf16_kernel<D, QB, BC, MINW, PRIO, NWAVES>;
+  const int64_t nwg = (int64_t)ntq * BH * nsplit;
+  auto kern = fwd_bf16_kernel<D, QB, BC, MINW, PRIO, NWAVES, SPLIT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(C::THREADS), C::LDS_BYTES, stream, q, k,
-                     v, o, lse, (int)N, ntq, scale * kLog2e);
+                     v, o, lse, (int)N, ntq, scale * kLog2e, nsplit, BH * N);
   return (int)hipGetLastError();
 }
 
@@ -293,8 +321,23 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   // d = 128: 8 waves x 32 query rows, key tiles of 128 (one workgroup per CU,
   // two waves per SIMD); d = 64: 4 waves x 32 rows, key tiles of 64.
   if (d == 128)
-    return launch<128, 1, 128, 2, true, 8>(q16, k16, v16, o16, lse, BH, N, scale, stream);
-  return launch<64, 1, 64, 2, false, 4>(q16, k16, v16, o16, lse, BH, N, scale, stream);
+    return launch<128, 1, 128, 2, true, 8>(q16, k16, v16, o16, lse, BH, N, scale, 1, stream);
+  return launch<64, 1, 64, 2, false, 4>(q16, k16, v16, o16, lse, BH, N, scale, 1, stream);
+}
+
+int fwd_split_tile(int64_t d) { return d == 128 ? 128 : 64; }
+
+int launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* o_part,
+                          float* lse_part, int64_t BH, int64_t N, int64_t d, float scale,
+                          int nsplit, hipStream_t stream) {
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* k16 = static_cast<const uint16_t*>(k);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  if (d == 128)
+    return launch<128, 1, 128, 2, true, 8, true>(q16, k16, v16, o_part, lse_part, BH, N, scale,
+                                                 nsplit, stream);
+  return launch<64, 1, 64, 2, false, 4, true>(q16, k16, v16, o_part, lse_part, BH, N, scale,
+                                              nsplit, stream);
 }
 
 }  // namespace fa

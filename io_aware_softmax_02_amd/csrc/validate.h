@@ -97,6 +97,24 @@ inline size_t bwd_workspace_bytes(const Shape& s, bool bf16) {
   return round_up(static_cast<size_t>(s.rows()) * sizeof(float), 256);
 }
 
+// Split-KV forward: n_split contiguous ranges of whole key tiles of `tile`
+// keys, at least one tile per range.
+inline int64_t split_max(const Shape& s, int64_t tile) {
+  if (check_shape(s, true) != FA_OK) return -1;
+  if (s.empty()) return 0;
+  return (s.N + tile - 1) / tile;
+}
+
+// n_split partial tensors of the shape: the count must be >= 1 and the
+// partials must stay inside the size limits (and the grid inside int32).
+inline fa_status check_parts(const Shape& s, int64_t n_split) {
+  if (n_split < 1) return FA_ERR_SHAPE;
+  if (s.empty()) return FA_OK;
+  if (n_split > kMaxElems / s.elems()) return FA_ERR_SHAPE;
+  if (s.B * s.H * ((s.N + 7) / 8) > ((int64_t(1) << 31) - 1) / n_split) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 inline fa_status check_workspace(const void* ws, size_t bytes, size_t need) {
   if (need == 0) return FA_OK;
   if (ws == nullptr) return FA_ERR_NULL;

@@ -11,6 +11,9 @@ leaves in its output directory into the short text summaries that are kept:
       HBM bytes per launch from FETCH_SIZE / WRITE_SIZE passes, calibrated
       against a 512 MiB device copy made in the same process (bench.py makes
       one before its timed region); bench.py reads OUT_JSON
+  python -m io_aware_softmax_02_amd.profile_summary sweep LOG
+  python -m io_aware_softmax_02_amd.profile_summary splitkv LOG
+      the JSON lines of `bench.py --sweep` / `bench.py --splitkv` as markdown
 """
 from __future__ import annotations
 
@@ -116,6 +119,50 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
     return doc
 
 
+def _json_lines(path: str) -> list:
+    return [json.loads(line) for line in open(path) if line.startswith("{")]
+
+
+def sweep_md(path: str) -> str:
+    out = ["# Sequence-length sweep (bf16, B = 1, H = 16, d = 128)\n",
+           "Command (repository root, one MI355X): `python bench.py --sweep > LOG; "
+           "python -m io_aware_softmax_02_amd.profile_summary sweep LOG`\n",
+           "Times are the median of several runs of back-to-back launches (HIP events on the "
+           "launch stream). fwd+bwd TF/s counts 14·B·H·N²·d over fa_fwd + fa_bwd. `extra bytes` "
+           "is the device memory the forward allocates beyond its inputs and outputs (torch "
+           "peak-allocation counter); `fp32 S per head` is what one materialised score matrix "
+           "would take.\n",
+           "| N | fwd µs | fwd TF/s | bwd ms | fwd+bwd TF/s | extra bytes | inputs+outputs MB | fp32 S per head |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in _json_lines(path):
+        b = r["fp32_scores_per_head_bytes"]
+        size = f"{b / 2**30:.2f} GiB" if b >= 2**30 else f"{b / 2**20:.0f} MiB"
+        out.append(f"| {r['N']} | {r['ms_fwd'] * 1e3:.0f} | {r['fwd_tflops']} | {r['ms_bwd']:.2f} | "
+                   f"{r['fwdbwd_tflops']} | {r['fwd_peak_extra_bytes']} | "
+                   f"{r['inputs_outputs_bytes_fwd'] / 1e6:.1f} | {size} |")
+    return "\n".join(out) + "\n"
+
+
+def splitkv_md(path: str) -> str:
+    out = ["# Split-KV forward + merge against the plain forward (bf16, d = 128)\n",
+           "Command (repository root, one MI355X): `python bench.py --splitkv > LOG; "
+           "python -m io_aware_softmax_02_amd.profile_summary splitkv LOG`\n",
+           "Median of five runs of 10 back-to-back launches, HIP events on the launch stream. "
+           "`split` is `fa_fwd_split` (fp32 partial O and LSE per key range), `merge` is "
+           "`fa_merge`; TF/s counts 4·B·H·N²·d over split + merge. The merge's bytes per "
+           "launch are n_split·rows·(4d+4) read + rows·(2d+4) written; its bound is HBM "
+           "(8 TB/s published).\n"]
+    for r in _json_lines(path):
+        out.append(f"\n## B={r['B']} H={r['H']} N={r['N']}: plain fa_fwd {r['plain_ms'] * 1e3:.1f} µs "
+                   f"= {r['plain_tflops']} TF/s\n")
+        out.append("| n_split | split µs | merge µs | total TF/s | merge GB/s | merge / HBM peak |")
+        out.append("|---|---|---|---|---|---|")
+        for x in r["splits"]:
+            out.append(f"| {x['n_split']} | {x['split_ms'] * 1e3:.1f} | {x['merge_ms'] * 1e3:.1f} | "
+                       f"{x['total_tflops']} | {x['merge_GBps']} | {x['merge_frac_of_hbm']} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv: list[str]) -> int:
     if len(argv) < 2:
         print(__doc__)
@@ -125,6 +172,10 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(trace(argv[2], argv[3], argv[4]))
     elif cmd == "counters":
         sys.stdout.write(counters(argv[2], argv[3], argv[4]))
+    elif cmd == "sweep":
+        sys.stdout.write(sweep_md(argv[2]))
+    elif cmd == "splitkv":
+        sys.stdout.write(splitkv_md(argv[2]))
     elif cmd == "traffic":
         doc = traffic(argv[2], argv[3], argv[4])
         for k, v in doc["kernels"].items():

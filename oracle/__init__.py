@@ -29,5 +29,8 @@ from .attention import (  # noqa: F401
     online_forward_normalised_head,
     two_pass_forward_head,
     softmax_rows,
+    split_bounds,
+    sdpa_split_head,
+    merge_parts,
 )
 from .brute import brute_forward, brute_backward  # noqa: F401

@@ -43,6 +43,9 @@ __all__ = [
     "online_forward_head",
     "online_forward_normalised_head",
     "two_pass_forward_head",
+    "split_bounds",
+    "sdpa_split_head",
+    "merge_parts",
 ]
 
 
@@ -234,3 +237,59 @@ def two_pass_forward_head(q, k, v, scale: float, block: int = 8,
         Sb = float(scale) * (q @ k[a:b].T)
         O += (np.exp(Sb - m[:, None]) / l[:, None]) @ v[a:b]
     return O, m + np.log(l)
+
+
+# ---------------------------------------------------------------------------
+# Split-KV partial results and their merge.
+#
+# A key range's forward is the plain definition restricted to those keys; the
+# merge is the rescale identity of [P3] "兩大核心魔法" (e^{x-m_new} =
+# e^{x-m_old} e^{m_old-m_new}) applied to whole ranges: with weights
+# e^{LSE_p - LSE}, the ranges' normalised outputs add up to the full one.
+# [P1] section 四: accounts kept separately combine without conflict, so the
+# order of the parts does not matter.
+# ---------------------------------------------------------------------------
+
+
+def split_bounds(n: int, n_split: int, tile: int) -> list:
+    """Key ranges [a, b) of a split forward: the keys are cut into whole
+    tiles of ``tile`` keys (the last one may be short), T = ceil(n / tile),
+    and range p holds tiles [p*T//n_split, (p+1)*T//n_split) (the rule the
+    library's header states for fa_fwd_split)."""
+    t = -(-n // tile)
+    if not 1 <= n_split <= t:
+        raise ValueError("need 1 <= n_split <= number of key tiles")
+    out = []
+    for p in range(n_split):
+        a, b = p * t // n_split, (p + 1) * t // n_split
+        out.append((a * tile, min(n, b * tile)))
+    return out
+
+
+def sdpa_split_head(q, k, v, scale: float, bounds) -> Tuple[np.ndarray, np.ndarray]:
+    """One head: the plain forward on each key range.  Returns (O_parts
+    [P, Nq, dv], LSE_parts [P, Nq])."""
+    outs = [sdpa_forward_head(q, _f64(k)[a:b], _f64(v)[a:b], scale) for a, b in bounds]
+    return np.stack([o for o, _ in outs]), np.stack([l for _, l in outs])
+
+
+def merge_parts(o_parts, lse_parts) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge of partial results over the leading axis.  o_parts [P, ..., dv],
+    lse_parts [P, ...].  LSE = m + ln sum_p e^{LSE_p - m} (m = max_p LSE_p) and
+    O = sum_p e^{LSE_p - LSE} O_p.  A part with LSE_p = -inf has weight 0 and
+    is skipped (whatever its O_p); rows whose parts are all -inf get O = 0 and
+    LSE = -inf."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    m = lse_parts.max(axis=0)
+    has = m > -np.inf                      # rows with at least one live part
+    m0 = np.where(has, m, 0.0)
+    total = np.zeros(m.shape)
+    for p in range(lse_parts.shape[0]):
+        total += np.exp(lse_parts[p] - m0)   # exp(-inf) = 0
+    lse = np.where(has, m0 + np.log(np.where(has, total, 1.0)), -np.inf)
+    o = np.zeros(o_parts.shape[1:])
+    for p in range(o_parts.shape[0]):
+        live = lse_parts[p] > -np.inf
+        w = np.where(live, np.exp(lse_parts[p] - np.where(has, lse, 0.0)), 0.0)
+        o += w[..., None] * np.where(live[..., None], o_parts[p], 0.0)
+    return o, lse

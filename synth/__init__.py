@@ -109,6 +109,24 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
     return q, k, v, dO
 
 
+def make_parts(P: int, B: int, H: int, N: int, d: int, seed: int, dead_every: int = 0):
+    """Seeded partial results for merge tests: o_part fp32 N(0,1)
+    [P,B,H,N,d], lse_part fp32 3*N(0,1) [P,B,H,N].  With dead_every = k > 0,
+    every k-th (part, row) entry gets lse = -inf and a NaN output row (a
+    part with no key), and the last row of every head is dead in all parts."""
+    g = torch.Generator().manual_seed(seed)
+    o = torch.randn((P, B, H, N, d), generator=g)
+    lse = 3.0 * torch.randn((P, B, H, N), generator=g)
+    if dead_every:
+        flat = lse.view(-1)
+        dead = torch.arange(0, flat.numel(), dead_every)
+        flat[dead] = -math.inf
+        o.view(-1, d)[dead] = math.nan
+        lse[..., N - 1] = -math.inf
+        o[..., N - 1, :] = math.nan
+    return o, lse
+
+
 def sampled_rows(w: Workload) -> np.ndarray:
     """Query rows checked per head for the very long workload.
 

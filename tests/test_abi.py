@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_expected_calls():
     names = declared_functions()
     for n in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_bwd_f32",
-              "fa_status_str", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
+              "fa_status_str", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+              "fa_fwd_split_max", "fa_fwd_split", "fa_merge"):
         assert n in names
 
 
@@ -95,6 +96,48 @@ def test_fwd_argument_checks(lib):
     # sizes whose element count overflows the accepted range
     assert fwd(lib, B=1 << 20, H=1 << 20, N=1 << 20) == L.FA_ERR_SHAPE
     assert fwd(lib, N=1 << 31) == L.FA_ERR_SHAPE
+
+
+def test_split_and_merge_argument_checks(lib):
+    from io_aware_softmax_02_amd import _lib as L
+
+    def split(ptrs=None, n=2, N=1000, d=128, scale=0.1):
+        q, k, v, op, lp = ptrs if ptrs is not None else P[:5]
+        return lib.fa_fwd_split(q, k, v, op, lp, 1, 1, N, d, scale, n, None)
+
+    def merge(ptrs=None, n=2, N=64, d=128):
+        op, lp, o, lse = ptrs if ptrs is not None else P[:4]
+        return lib.fa_merge(op, lp, n, o, lse, 1, 1, N, d, None)
+
+    # key tiles are 128 keys at d = 128 and 64 at d = 64
+    assert lib.fa_fwd_split_max(1, 1, 1000, 128) == 8
+    assert lib.fa_fwd_split_max(1, 1, 1000, 64) == 16
+    assert lib.fa_fwd_split_max(1, 1, 1, 128) == 1
+    assert lib.fa_fwd_split_max(1, 1, 0, 128) == 0
+    assert lib.fa_fwd_split_max(1, 1, 10, 96) == -1
+    assert lib.fa_fwd_split_max(1, 1, -1, 128) == -1
+    assert split(n=0) == L.FA_ERR_SHAPE
+    assert split(n=-3) == L.FA_ERR_SHAPE
+    assert split(n=9) == L.FA_ERR_SHAPE
+    # the largest allowed count passes the count check and stops at the next
+    # one (a NULL pointer), so nothing is launched on these fake addresses
+    assert split(ptrs=[P[0], P[1], P[2], P[3], 0], n=16, d=64) == L.FA_ERR_NULL
+    assert split(ptrs=[P[0], P[1], P[2], 0, P[4]]) == L.FA_ERR_NULL
+    assert split(ptrs=[P[0], P[1], P[2], P[3] + 4, P[4]]) == L.FA_ERR_ALIGN
+    assert split(d=96) == L.FA_ERR_UNSUPPORTED
+    assert split(scale=0.0) == L.FA_ERR_SCALE
+    # o_part (2 x 1000 x 128 x 4 B) reaching into lse_part, and o_part on q
+    assert split(ptrs=[P[0], P[1], P[2], P[3], P[3] + 2 * 1000 * 128 * 4 - 16]) == L.FA_ERR_ALIAS
+    assert split(ptrs=[P[0], P[1], P[2], P[0] + 16, P[4]]) == L.FA_ERR_ALIAS
+    assert merge(n=0) == L.FA_ERR_SHAPE
+    assert merge(ptrs=[P[0], 0, P[2], P[3]]) == L.FA_ERR_NULL
+    assert merge(ptrs=[P[0], P[1], P[2] + 8, P[3]]) == L.FA_ERR_ALIGN
+    assert merge(d=32) == L.FA_ERR_UNSUPPORTED
+    # output o overlapping the (2 x 64 x 128 x 4 B) o_part input
+    assert merge(ptrs=[P[0], P[1], P[0] + 2 * 64 * 128 * 4 - 16, P[3]]) == L.FA_ERR_ALIAS
+    # empty problems: nothing to do, pointers may be NULL
+    assert lib.fa_fwd_split(0, 0, 0, 0, 0, 1, 1, 0, 128, 0.1, 1, None) == L.FA_OK
+    assert lib.fa_merge(0, 0, 3, 0, 0, 0, 4, 64, 128, None) == L.FA_OK
 
 
 def test_empty_problems_are_noops(lib):

@@ -388,3 +388,91 @@ def _bwd_mutant(change):
                                     "dV_no_transpose", "dQ_no_scale"])
 def test_planted_backward_mistake_is_caught(change):
     assert _bwd_checks(_bwd_mutant(change)) != []
+
+
+# ---------------------------------------------------------------------------
+# Split-KV parts and their merge ([P3] "兩大核心魔法" rescale identity applied
+# to whole key ranges; [P1] section 四: the ranges combine in any order).
+# ---------------------------------------------------------------------------
+
+def _merge_checks(merge, split_head=A.sdpa_split_head):
+    """Merge pins.  merge(o_parts, lse_parts) -> (O, LSE)."""
+    bad = []
+    # 1. Hand-worked: two parts with LSE ln 2 and ln 6 -> LSE ln 8, weights
+    #    2/8 and 6/8.
+    o, l = merge(np.array([[[1.0, 0.0]], [[0.0, 1.0]]]), np.array([[math.log(2)], [math.log(6)]]))
+    if abs(l[0] - math.log(8)) > 1e-15 or np.abs(o[0] - [0.25, 0.75]).max() > 1e-15:
+        bad.append("hand-worked two-part merge")
+    # 2. The merge of the parts equals the plain forward on all keys, for
+    #    ragged N and every split count (closed-form identity, no tolerance
+    #    beyond float64 rounding).
+    for n, tile in ((37, 8), (64, 8), (9, 4)):
+        q, k, v = rnd((5, 6), 1), rnd((n, 6), 2, 1.5), rnd((n, 3), 3)
+        O, L = A.sdpa_forward_head(q, k, v, 0.4)
+        for p in range(1, -(-n // tile) + 1):
+            op, lp = split_head(q, k, v, 0.4, A.split_bounds(n, p, tile))
+            o, l = merge(op, lp)
+            if np.abs(o - O).max() > 1e-12 or np.abs(l - L).max() > 1e-12:
+                bad.append(f"merge of {p} parts != full forward (n={n})")
+                break
+    # 3. Order of the parts does not matter.
+    op, lp = A.sdpa_split_head(rnd((4, 5), 4), rnd((40, 5), 5), rnd((40, 5), 6), 0.7,
+                               A.split_bounds(40, 5, 8))
+    perm = [3, 0, 4, 2, 1]
+    o1, l1 = merge(op, lp)
+    o2, l2 = merge(op[perm], lp[perm])
+    if np.abs(o1 - o2).max() > 1e-13 or np.abs(l1 - l2).max() > 1e-13:
+        bad.append("merge depends on the order of the parts")
+    # 4. One part: identity.
+    o, l = merge(op[:1], lp[:1])
+    if np.abs(o - op[0]).max() > 0 or np.abs(l - lp[0]).max() > 0:
+        bad.append("single-part merge is not the identity")
+    # 5. A part with LSE = -inf contributes nothing, whatever its O holds.
+    o, l = merge(np.array([[[np.nan, 7.0]], [[0.5, 1.0]]]), np.array([[-np.inf], [0.3]]))
+    if not (np.isfinite(o).all() and np.abs(o[0] - [0.5, 1.0]).max() == 0 and l[0] == 0.3):
+        bad.append("-inf part not skipped")
+    return bad
+
+
+def test_merge_pins():
+    assert _merge_checks(A.merge_parts) == []
+
+
+def test_split_bounds_rule():
+    # Whole tiles, every range non-empty, ranges cover [0, N) in order.
+    for n, tile in ((8192, 128), (1000, 64), (1, 128), (129, 128)):
+        t = -(-n // tile)
+        for p in range(1, t + 1):
+            b = A.split_bounds(n, p, tile)
+            assert b[0][0] == 0 and b[-1][1] == n
+            assert all(x[1] == y[0] for x, y in zip(b, b[1:]))
+            assert all(a < c for a, c in b)
+            assert all(a % tile == 0 for a, _ in b)
+    with pytest.raises(ValueError):
+        A.split_bounds(100, 0, 64)
+    with pytest.raises(ValueError):
+        A.split_bounds(100, 3, 64)
+
+
+def _mut_merge_plain_average(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, float), np.asarray(lse_parts, float)
+    m = lse_parts.max(axis=0)
+    return o_parts.mean(axis=0), m + np.log(np.exp(lse_parts - m).sum(axis=0))
+
+
+def _mut_merge_weights_unnormalised(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, float), np.asarray(lse_parts, float)
+    m = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - m)
+    return (w[..., None] * o_parts).sum(axis=0), m + np.log(w.sum(axis=0))
+
+
+def _mut_merge_lse_max_only(o_parts, lse_parts):
+    o, _ = A.merge_parts(o_parts, lse_parts)
+    return o, np.asarray(lse_parts, float).max(axis=0)
+
+
+@pytest.mark.parametrize("mutant", [_mut_merge_plain_average, _mut_merge_weights_unnormalised,
+                                    _mut_merge_lse_max_only], ids=lambda f: f.__name__)
+def test_planted_merge_mistake_is_caught(mutant):
+    assert _merge_checks(mutant) != []
