@@ -18,6 +18,9 @@ Two further measurements print one JSON line per case instead:
                                  (d = 128, H = 16), with peak device memory
     python bench.py --splitkv   split-KV forward + merge against the plain
                                  forward when B*H is small
+    python bench.py --contrast  standard attention through device memory
+                                 (S, then P, then O, with torch's own GEMM and
+                                 softmax) beside fa_fwd, for contrast only
 """
 
 from __future__ import annotations
@@ -55,6 +58,8 @@ def parse():
                     help="sequence-length sweep instead of the headline measurement")
     ap.add_argument("--splitkv", action="store_true",
                     help="split-KV forward + merge measurement instead of the headline one")
+    ap.add_argument("--contrast", action="store_true",
+                    help="materialised standard attention beside fa_fwd instead of the headline")
     return ap.parse_args()
 
 
@@ -217,6 +222,82 @@ def splitkv(args):
         print(json.dumps(res), flush=True)
 
 
+def contrast(args):
+    """Standard attention as three steps through device memory, for contrast
+    with the tiled kernel (no part of the library): S = (s Q) K^T written as an
+    N x N bf16 matrix per head, P = softmax(S) read and written again, O = P V.
+    torch's GEMM and softmax kernels do the work.  Reported per step: time
+    (median of back-to-back launches), the bytes of the N x N tensors it
+    moves, and the peak device memory of the whole sequence, beside fa_fwd on
+    the same inputs."""
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    # calibration copy for counter-based traffic (see the headline run)
+    cal_src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    for name in ("fwd_bf16_b4h16_n2048_d64", "long_bf16_b1h16_n8192_d128"):
+        w = synth.WORKLOADS[name]
+        q, k, v, _ = (x.to(dev) if x is not None else None for x in synth.make_inputs(w))
+        B, H, N, d, sc = w.B, w.H, w.N, w.d, w.scale
+        # The right operand of a batched bf16 product is made contiguous first.
+        kt = k.transpose(-1, -2).contiguous()
+        qs = q * sc
+        S = torch.empty(B, H, N, N, dtype=torch.bfloat16, device=dev)
+        P = torch.empty_like(S)
+        O = torch.empty_like(q)
+        step_s = lambda: torch.matmul(qs, kt, out=S)
+        step_p = lambda: torch.softmax(S, dim=-1, out=P)
+        step_o = lambda: torch.matmul(P, v, out=O)
+        for f in (step_s, step_p, step_o):
+            f()
+        torch.cuda.synchronize()
+        inner = 10
+        ms = [median_time(f, inner, stream) for f in (step_s, step_p, step_o)]
+        # peak memory of one pass, from nothing but the inputs
+        del S, P
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        S2 = torch.matmul(qs, kt)
+        P2 = torch.softmax(S2, dim=-1)
+        O2 = torch.matmul(P2, v)
+        torch.cuda.synchronize()
+        peak_std = torch.cuda.max_memory_allocated() - base
+        del S2, P2
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o_fa, l_fa = fa.fa_fwd(q, k, v, sc)
+        torch.cuda.synchronize()
+        peak_fa = torch.cuda.max_memory_allocated() - base
+        ms_fa = median_time(lambda: fa.fa_fwd(q, k, v, sc, o=o_fa, lse=l_fa), inner, stream)
+        diff = float((O2.float() - o_fa.float()).abs().max())
+        nn = B * H * N * N * 2
+        gemm_flop = 2.0 * B * H * N * N * d
+        print(json.dumps({
+            "contrast": name, "B": B, "H": H, "N": N, "d": d,
+            "ms_S_gemm": round(ms[0], 4), "ms_softmax": round(ms[1], 4), "ms_PV_gemm": round(ms[2], 4),
+            "ms_standard_total": round(sum(ms), 4), "ms_fa_fwd": round(ms_fa, 4),
+            "gemm_time_fraction": round((ms[0] + ms[2]) / sum(ms), 3),
+            "S_gemm_tflops": round(gemm_flop / (ms[0] * 1e-3) / 1e12, 1),
+            "PV_gemm_tflops": round(gemm_flop / (ms[2] * 1e-3) / 1e12, 1),
+            "softmax_GBps_of_NxN_traffic": round(2 * nn / (ms[1] * 1e-3) / 1e9, 1),
+            "nxn_bytes_per_tensor": nn,
+            "peak_extra_bytes_standard": int(peak_std), "peak_extra_bytes_fa_fwd": int(peak_fa),
+            "max_abs_diff_O_standard_vs_fa_fwd": round(diff, 5),
+        }), flush=True)
+        del q, k, v, kt, qs, O, O2, o_fa, l_fa
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -228,6 +309,8 @@ def main():
         return sweep(args)
     if args.splitkv:
         return splitkv(args)
+    if args.contrast:
+        return contrast(args)
 
     import torch
     import io_aware_softmax_02_amd as fa

@@ -11,6 +11,10 @@ leaves in its output directory into the short text summaries that are kept:
       HBM bytes per launch from FETCH_SIZE / WRITE_SIZE passes, calibrated
       against a 512 MiB device copy made in the same process (bench.py makes
       one before its timed region); bench.py reads OUT_JSON
+  python -m io_aware_softmax_02_amd.profile_summary traffic-table FETCH_CSV WRITE_CSV TITLE COMMAND
+      calibrated HBM bytes per dispatch of every kernel in a run, as markdown
+  python -m io_aware_softmax_02_amd.profile_summary contrast LOG
+      the JSON lines of `bench.py --contrast` as markdown
   python -m io_aware_softmax_02_amd.profile_summary sweep LOG
   python -m io_aware_softmax_02_amd.profile_summary splitkv LOG
       the JSON lines of `bench.py --sweep` / `bench.py --splitkv` as markdown
@@ -40,7 +44,9 @@ TRAFFIC_SOURCES = ["io_aware_softmax_02_amd/csrc/" + x for x in
 
 
 def short(name: str) -> str:
-    return re.sub(r"\(.*", "", name.replace("void ", "").replace("fa::(anonymous namespace)::", ""))
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    name = re.sub(r"^fa::", "", name)          # the library's own kernels
+    return re.sub(r"\(.*", "", name)
 
 
 def source_digests() -> dict:
@@ -74,6 +80,20 @@ def per_dispatch(path: str) -> dict:
     return {k: {c: sum(d.values()) / len(d) for c, d in cs.items()} for k, cs in agg.items()}
 
 
+def calibration(path: str, counter: str) -> float:
+    """The counter's value on the calibration copy: the device-copy dispatches
+    with the largest grid (other copies in the run, e.g. scalar read-backs,
+    are tiny)."""
+    rows = [r for r in csv.DictReader(open(path))
+            if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    top = max(int(r["Grid_Size"]) for r in rows)
+    per = collections.defaultdict(float)
+    for r in rows:
+        if int(r["Grid_Size"]) == top:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return sum(per.values()) / len(per)
+
+
 def counters(path: str, title: str, cmd: str) -> str:
     data = per_dispatch(path)
     names = sorted({c for cs in data.values() for c in cs})
@@ -90,9 +110,9 @@ def counters(path: str, title: str, cmd: str) -> str:
 def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
     f = {k: v["FETCH_SIZE"] for k, v in per_dispatch(fetch_csv).items() if "FETCH_SIZE" in v}
     w = {k: v["WRITE_SIZE"] for k, v in per_dispatch(write_csv).items() if "WRITE_SIZE" in v}
-    copy = next(k for k in f if "copyBuffer" in k)
-    rf = COPY_BYTES / (f[copy] * 1024.0)
-    wf = COPY_BYTES / (w[copy] * 1024.0)
+    cf, cw = calibration(fetch_csv, "FETCH_SIZE"), calibration(write_csv, "WRITE_SIZE")
+    rf = COPY_BYTES / (cf * 1024.0)
+    wf = COPY_BYTES / (cw * 1024.0)
     sha = source_digests()
     kern = {}
     for k in f:
@@ -105,8 +125,8 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
     doc = {"what": "HBM traffic per launch at B=1 H=16 N=8192 d=128, from rocprofv3 FETCH_SIZE "
                    "and WRITE_SIZE (KiB per dispatch), each scaled by the same counter on a "
                    "512 MiB device copy run in the same bench process",
-           "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": f[copy],
-                           "write_size_kib": w[copy], "read_factor": rf, "write_factor": wf},
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": cf,
+                           "write_size_kib": cw, "read_factor": rf, "write_factor": wf},
            "commands": [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} --kernel-include-regex '{rx}' "
                         f"-f csv -d gpurun_out/pmc_{t} -o pmc -- python3 bench.py --steps 2 "
                         f"--warmup 1 --no-cpu-baseline" for c, t in (("FETCH_SIZE", "F"), ("WRITE_SIZE", "W"))]
@@ -119,8 +139,45 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
     return doc
 
 
+def traffic_table(fetch_csv: str, write_csv: str, title: str, cmd: str) -> str:
+    fs, ws = per_dispatch(fetch_csv), per_dispatch(write_csv)
+    f = {k: v["FETCH_SIZE"] for k, v in fs.items() if "FETCH_SIZE" in v}
+    w = {k: v["WRITE_SIZE"] for k, v in ws.items() if "WRITE_SIZE" in v}
+    rf = COPY_BYTES / (calibration(fetch_csv, "FETCH_SIZE") * 1024.0)
+    wf = COPY_BYTES / (calibration(write_csv, "WRITE_SIZE") * 1024.0)
+    calls = collections.Counter()
+    for r in csv.DictReader(open(fetch_csv)):
+        calls[short(r["Kernel_Name"])] += 1
+    out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n",
+           f"```\n{cmd}\n```\n",
+           f"HBM bytes per dispatch: FETCH_SIZE x {rf:.3f} and WRITE_SIZE x {wf:.3f} (factors from "
+           f"a {COPY_BYTES >> 20} MiB device copy in the same process), averaged over dispatches.\n",
+           "| kernel | read MB | written MB |", "|---|---|---|"]
+    for k in sorted(f, key=lambda x: -f[x]):
+        if "copyBuffer" in k:
+            continue
+        name = k if len(k) <= 70 else k[:67] + "..."
+        out.append(f"| `{name}` | {f[k] * 1024 * rf / 1e6:.1f} | {w.get(k, 0) * 1024 * wf / 1e6:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def _json_lines(path: str) -> list:
     return [json.loads(line) for line in open(path) if line.startswith("{")]
+
+
+def contrast_md(path: str) -> str:
+    out = ["| shape | S = QKᵀ GEMM µs | softmax µs | O = PV GEMM µs | standard total µs | GEMM share of time | "
+           "fa_fwd µs | speed-up | N×N bytes per tensor | extra memory, standard | extra memory, fa_fwd | "
+           "max abs O difference |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in _json_lines(path):
+        out.append(f"| B={r['B']} H={r['H']} N={r['N']} d={r['d']} | {r['ms_S_gemm'] * 1e3:.0f} | "
+                   f"{r['ms_softmax'] * 1e3:.0f} | {r['ms_PV_gemm'] * 1e3:.0f} | "
+                   f"{r['ms_standard_total'] * 1e3:.0f} | {r['gemm_time_fraction']:.0%} | "
+                   f"{r['ms_fa_fwd'] * 1e3:.0f} | {r['ms_standard_total'] / r['ms_fa_fwd']:.1f}x | "
+                   f"{r['nxn_bytes_per_tensor'] / 1e9:.2f} GB | {r['peak_extra_bytes_standard'] / 1e9:.2f} GB | "
+                   f"{r['peak_extra_bytes_fa_fwd'] / 1e6:.1f} MB | {r['max_abs_diff_O_standard_vs_fa_fwd']} |")
+    return "\n".join(out) + "\n"
 
 
 def sweep_md(path: str) -> str:
@@ -172,6 +229,10 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(trace(argv[2], argv[3], argv[4]))
     elif cmd == "counters":
         sys.stdout.write(counters(argv[2], argv[3], argv[4]))
+    elif cmd == "traffic-table":
+        sys.stdout.write(traffic_table(argv[2], argv[3], argv[4], argv[5]))
+    elif cmd == "contrast":
+        sys.stdout.write(contrast_md(argv[2]))
     elif cmd == "sweep":
         sys.stdout.write(sweep_md(argv[2]))
     elif cmd == "splitkv":
