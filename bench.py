@@ -18,6 +18,8 @@ Two further measurements print one JSON line per case instead:
                                  (d = 128, H = 16), with peak device memory
     python bench.py --splitkv   split-KV forward + merge against the plain
                                  forward when B*H is small
+    python bench.py --fp32      the fp32 path (fa_fwd_f32, fa_bwd_f32) at several
+                                 sizes, against the fp32 peak
     python bench.py --contrast  standard attention through device memory
                                  (S, then P, then O, with torch's own GEMM and
                                  softmax) beside fa_fwd, for contrast only
@@ -58,6 +60,8 @@ def parse():
                     help="sequence-length sweep instead of the headline measurement")
     ap.add_argument("--splitkv", action="store_true",
                     help="split-KV forward + merge measurement instead of the headline one")
+    ap.add_argument("--fp32", action="store_true",
+                    help="fp32 path measurement instead of the headline one")
     ap.add_argument("--contrast", action="store_true",
                     help="materialised standard attention beside fa_fwd instead of the headline")
     return ap.parse_args()
@@ -222,6 +226,44 @@ def splitkv(args):
         print(json.dumps(res), flush=True)
 
 
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and packed vector), published
+
+
+def fp32(args):
+    """Throughput of the fp32 path (fa_fwd_f32 / fa_bwd_f32) on seeded
+    N(0,1) inputs, against the published fp32 peak."""
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    for B, H, N, d in ((1, 1, 64, 64), (1, 16, 2048, 64), (1, 16, 4096, 128), (1, 16, 8192, 128)):
+        q, k, v, dO = (x.to(dev) for x in synth.make_qkv(B, H, N, d, torch.float32, seed=9,
+                                                        backward=True))
+        s = synth.default_scale(d)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(max(fa.fa_bwd_f32_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
+                         device=dev)
+        fwd = lambda: fa.fa_fwd_f32(q, k, v, s, o=o, lse=lse)
+        bwd = lambda: fa.fa_bwd_f32(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+        fwd(); bwd()
+        torch.cuda.synchronize()
+        inner = 20 if N <= 2048 else 3
+        mf = median_time(fwd, inner, stream, 3)
+        mb = median_time(bwd, inner, stream, 3)
+        fl = 4.0 * B * H * N * N * d
+        print(json.dumps({"fp32": True, "B": B, "H": H, "N": N, "d": d,
+                          "ms_fwd": round(mf, 4), "ms_bwd": round(mb, 4),
+                          "fwd_tflops": round(fl / (mf * 1e-3) / 1e12, 2),
+                          "fwdbwd_tflops": round(3.5 * fl / ((mf + mb) * 1e-3) / 1e12, 2),
+                          "fwd_frac_of_fp32_peak": round(fl / (mf * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}),
+              flush=True)
+        del q, k, v, dO, o, lse, dq, dk, dv, ws
+
+
 def contrast(args):
     """Standard attention as three steps through device memory, for contrast
     with the tiled kernel (no part of the library): S = (s Q) K^T written as an
@@ -311,6 +353,8 @@ def main():
         return splitkv(args)
     if args.contrast:
         return contrast(args)
+    if args.fp32:
+        return fp32(args)
 
     import torch
     import io_aware_softmax_02_amd as fa

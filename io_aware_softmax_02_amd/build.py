@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libfa_mi355x.so"
 LIB = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "attn_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_merge.hip"]
+SOURCES = ["api.cpp", "attn_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_merge.hip",
+           "attn_f32_mfma.hip"]
 # The backward kernels keep their matrix-core accumulators in arch VGPRs
 # (instead of the AGPR form the compiler picks when a kernel needs more than
 # 256 registers): the score and dP accumulators feed VALU work every tile,

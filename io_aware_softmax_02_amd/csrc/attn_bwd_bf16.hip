@@ -36,12 +36,6 @@ constexpr int kStepAhead = 4;
 constexpr int kDkdvStepAhead = 4;
 constexpr int kDkdvReadAhead = 3;
 
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-  const int x = wg & 7, idx = wg >> 3;
-  const int base = nwg >> 3, rem = nwg & 7;
-  return x * base + (x < rem ? x : rem) + idx;
-}
-
 // ---------------------------------------------------------------------------
 // Preprocess: D_i = sum_c dO_ic O_ic (fp32).  D/8 lanes per row, 16 B each.
 // ---------------------------------------------------------------------------

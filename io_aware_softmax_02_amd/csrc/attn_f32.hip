@@ -1,8 +1,8 @@
 // fp32 attention kernels: plain FMA arithmetic, natural exp, 8-query by 8-key
 // tiles, one wave per workgroup.  They follow the tiled recurrence with the
 // blocks of the fable of the 64 merchants (算珠楼的掌簿人, fable section 二: 64
-// rows cut into 8 stacks of 8) and serve tight checks at small sizes; the
-// bf16 kernels are the fast path.
+// rows cut into 8 stacks of 8) and take the head dims the matrix-core fp32
+// kernels (attn_f32_mfma.hip, d = 64 and 128) do not.
 //
 // Forward, per query row (账房先生的奔命, section 六; rescale identity of the
 // star-observatory fable page, section "兩大核心魔法"):
@@ -236,8 +236,14 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
 
 }  // namespace
 
+bool f32_mfma_ok(int64_t N, int64_t d);
+int launch_fwd_f32_mfma(const float* q, const float* k, const float* v, float* o, float* lse,
+                        int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
+
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
+  // d = 64, 128: matrix-core kernel (attn_f32_mfma.hip); other d: this file's.
+  if (f32_mfma_ok(N, d)) return launch_fwd_f32_mfma(q, k, v, o, lse, BH, N, d, scale, stream);
   const int ntq = (int)((N + T - 1) / T);
   hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)(ntq * BH)), dim3(64), 0, stream, q, k, v,
                      o, lse, (int)N, (int)d, ntq, scale);

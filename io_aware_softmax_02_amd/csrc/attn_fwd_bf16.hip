@@ -60,16 +60,6 @@ struct FwdCfg {
   static_assert(BC % 32 == 0 && BC <= 128, "key tile is a multiple of 32 rows");
 };
 
-// Maps the hardware workgroup id to a logical tile id so that consecutive
-// logical ids (the row tiles of one head) run on the same XCD: workgroups are
-// dealt to the 8 XCDs round-robin, and each XCD has its own L2, so the K/V
-// tiles of a head are then fetched into one L2 and reused there.
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-  const int x = wg & 7, idx = wg >> 3;
-  const int base = nwg >> 3, rem = nwg & 7;
-  return x * base + (x < rem ? x : rem) + idx;
-}
-
 template <int D, int QB, int BC, int MINW, bool PRIO, int NWAVES = 4, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

@@ -101,6 +101,16 @@ __device__ __forceinline__ float buf_loadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Maps the hardware workgroup id to a logical tile id so that consecutive
+// logical ids (the tiles of one head) run on the same XCD: workgroups are
+// dealt to the 8 XCDs round-robin, and each XCD has its own L2, so a head's
+// streamed tiles are fetched into one L2 and reused there.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+  const int x = wg & 7, idx = wg >> 3;
+  const int base = nwg >> 3, rem = nwg & 7;
+  return x * base + (x < rem ? x : rem) + idx;
+}
+
 // Lanes l and l ^ 32 exchange a value with v_permlane32_swap: called with
 // the same register twice, the two results hold x[l % 32] and x[l % 32 + 32]
 // in every lane (a VALU op, no LDS round trip).

@@ -77,8 +77,12 @@ def test_tiny_f32_forward():
     assert ea <= TOL_F32 and el <= TOL_F32
 
 
+# d = 64 and 128 run on the fp32 matrix-core kernels; the other head dims on
+# the FMA kernels.
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 1), (1, 2, 7, 3), (2, 1, 65, 64),
-                                     (1, 1, 100, 128), (1, 3, 33, 17), (1, 1, 9, 8)])
+                                     (1, 1, 100, 128), (1, 3, 33, 17), (1, 1, 9, 8),
+                                     (1, 1, 1, 128), (1, 2, 1000, 128), (2, 2, 513, 64),
+                                     (1, 2, 4096, 128)])
 def test_f32_forward_shapes(B, H, N, d):
     say(f"case f32 fwd B={B} H={H} N={N} d={d}")
     q, k, v, _ = synth.make_qkv(B, H, N, d, torch.float32, seed=100 + N + d)
