@@ -148,9 +148,11 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
 
 /* ------------------------------------------------------------------------ */
 /* fp32 path: every tensor is float32, 1 <= d <= 128, pointers 4-byte        */
-/* aligned.  Plain FMA arithmetic with natural exp, key blocks of 8 (the     */
-/* 8 stacks of 8 of 算珠楼的掌簿人, fable section 二).  Meant for tight checks  */
-/* of the method at small sizes rather than for speed.                       */
+/* aligned; no rounding anywhere (P and dS stay fp32).  d = 64 and 128 run   */
+/* on the fp32 matrix cores (key and query tiles of 32) when one head of one */
+/* tensor fits 2 GiB; other d use FMA kernels with key blocks of 8 (the 8     */
+/* stacks of 8 of 算珠楼的掌簿人, fable section 二).  Same method and          */
+/* citations as the bf16 calls.                                              */
 /* ------------------------------------------------------------------------ */
 
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

@@ -240,6 +240,10 @@ bool f32_mfma_ok(int64_t N, int64_t d);
 int launch_fwd_f32_mfma(const float* q, const float* k, const float* v, float* o, float* lse,
                         int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
 
+int launch_bwd_f32_mfma(const float* q, const float* k, const float* v, const float* lse,
+                        const float* dO, const float* delta, float* dq, float* dk, float* dv,
+                        int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
+
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
   // d = 64, 128: matrix-core kernel (attn_f32_mfma.hip); other d: this file's.
@@ -259,6 +263,8 @@ int launch_bwd_f32(const float* q, const float* k, const float* v, const float* 
                      stream, o, dO, delta, rows, (int)d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
+  if (f32_mfma_ok(N, d))
+    return launch_bwd_f32_mfma(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, d, scale, stream);
   const int nt = (int)((N + T - 1) / T);
   hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k,
                      v, lse, dO, delta, dk, dv, (int)N, (int)d, nt, scale);

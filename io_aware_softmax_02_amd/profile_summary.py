@@ -13,6 +13,8 @@ leaves in its output directory into the short text summaries that are kept:
       one before its timed region); bench.py reads OUT_JSON
   python -m io_aware_softmax_02_amd.profile_summary traffic-table FETCH_CSV WRITE_CSV TITLE COMMAND
       calibrated HBM bytes per dispatch of every kernel in a run, as markdown
+  python -m io_aware_softmax_02_amd.profile_summary fp32 LOG
+      the JSON lines of `bench.py --fp32` as markdown
   python -m io_aware_softmax_02_amd.profile_summary contrast LOG
       the JSON lines of `bench.py --contrast` as markdown
   python -m io_aware_softmax_02_amd.profile_summary sweep LOG
@@ -165,6 +167,21 @@ def _json_lines(path: str) -> list:
     return [json.loads(line) for line in open(path) if line.startswith("{")]
 
 
+def fp32_md(path: str) -> str:
+    out = ["# fp32 path (fa_fwd_f32, fa_bwd_f32)\n",
+           "Command (repository root, one MI355X): `python bench.py --fp32 > LOG; "
+           "python -m io_aware_softmax_02_amd.profile_summary fp32 LOG`\n",
+           "Median of three runs of back-to-back launches, HIP events on the launch stream. "
+           "d = 64 and 128 run on the fp32 matrix cores (v_mfma_f32_32x32x2_f32); the fp32 peak "
+           "is 157.3 TF/s (published). Counted work: 4·B·H·N²·d forward, 14·B·H·N²·d fwd+bwd.\n",
+           "| B | H | N | d | fwd ms | bwd ms | fwd TF/s | fwd share of fp32 peak | fwd+bwd TF/s |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in _json_lines(path):
+        out.append(f"| {r['B']} | {r['H']} | {r['N']} | {r['d']} | {r['ms_fwd']:.4f} | {r['ms_bwd']:.4f} | "
+                   f"{r['fwd_tflops']} | {r['fwd_frac_of_fp32_peak']:.1%} | {r['fwdbwd_tflops']} |")
+    return "\n".join(out) + "\n"
+
+
 def contrast_md(path: str) -> str:
     out = ["| shape | S = QKᵀ GEMM µs | softmax µs | O = PV GEMM µs | standard total µs | GEMM share of time | "
            "fa_fwd µs | speed-up | N×N bytes per tensor | extra memory, standard | extra memory, fa_fwd | "
@@ -231,6 +248,8 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(counters(argv[2], argv[3], argv[4]))
     elif cmd == "traffic-table":
         sys.stdout.write(traffic_table(argv[2], argv[3], argv[4], argv[5]))
+    elif cmd == "fp32":
+        sys.stdout.write(fp32_md(argv[2]))
     elif cmd == "contrast":
         sys.stdout.write(contrast_md(argv[2]))
     elif cmd == "sweep":
