@@ -25,8 +25,10 @@
 //   score accumulators already in the B-operand layout of O^T += V^T P^T, so
 //   P never touches LDS; the V^T operand is gathered from the V tile with
 //   transposing LDS reads in the matching key order.  Both tiles are stored
-//   in the order their reads consume them (lds_tile.h), so every LDS read is
-//   a base register plus an immediate offset.
+//   in row-segment order (lds_tile.h): every direct load reads whole 64-byte
+//   row segments, the rate at which the load path runs at full speed, and
+//   every LDS read is a base register (two for K) plus an immediate offset,
+//   free of bank conflicts.
 //   Base-2 domain: c = scale * log2(e); p = 2^(c s - m) with m in log2 units;
 //   LSE = ln 2 * (m + log2 l).
 //
@@ -112,20 +114,40 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
   const int nkt = (N + BC - 1) / BC;
   const int j0 = SPLIT ? (int)((int64_t)part * nkt / nsplit) : 0;
   const int j1 = SPLIT ? (int)((int64_t)(part + 1) * nkt / nsplit) : nkt;
-  rowop_load<D, BC, C::WAVES>(smem, rk, j0 * BC, wave, lane);
-  trop_load<D, BC, C::WAVES>(smem + C::TILE, rv, j0 * BC, wave, lane);
+  // K and V tiles in row-segment order (K swizzled for its row-operand
+  // reads, V plain for its transposing reads); buffer b at byte
+  // b * BUF_ELEMS * 2, K then V.
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t kvoff = seg_dma_voff<D, C::WAVES, true>(wave, lane);
+  const uint32_t vvoff = seg_dma_voff<D, C::WAVES, false>(wave, lane);
+  constexpr int NU = (BC / 16) * (D / 32) / C::WAVES;   // loads per tile and wave
+  static_assert(NU * C::WAVES == (BC / 16) * (D / 32), "whole loads per wave");
+  auto load_tile = [&](int jt, int b) {
+    uint32_t kd = lds0 + (uint32_t)(b * C::BUF_ELEMS * 2), vd = kd + (uint32_t)(C::TILE * 2);
+    const uint32_t r0 = (uint32_t)(jt * BC * D * 2);
+    asm volatile("" : "+s"(kd), "+s"(vd));   // one address per buffer, not one per load
+#pragma unroll
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, kvoff, r0, wave, u);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, vvoff, r0, wave, u);
+  };
+  const uint32_t kbase0 = seg_rowop_base<D>(lane, 0), kbase1 = seg_rowop_base<D>(lane, 1);
+  const uint32_t vbase = seg_trop_base<D>(lane);
+  load_tile(j0, 0);
   wait_vmem();
   __syncthreads();
 
   for (int j = j0; j < j1; ++j) {
     const int jb = (j - j0) & 1;   // buffer of tile j
-    const uint16_t* kl = smem + jb * C::BUF_ELEMS + 8 * lane;   // this lane's K reads
-    const uint16_t* vl = smem + jb * C::BUF_ELEMS + C::TILE + 4 * lane;
-    if (j + 1 < j1) {
-      uint16_t* nb = smem + (jb ^ 1) * C::BUF_ELEMS;
-      rowop_load<D, BC, C::WAVES>(nb, rk, (j + 1) * BC, wave, lane);
-      trop_load<D, BC, C::WAVES>(nb + C::TILE, rv, (j + 1) * BC, wave, lane);
-    }
+    uint32_t bo = (uint32_t)(jb * C::BUF_ELEMS * 2);
+    asm volatile("" : "+s"(bo));
+    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(smem) + bo;
+    const uint8_t* kl[2] = {kb8 + kbase0, kb8 + kbase1};   // this lane's K reads
+    const uint8_t* vl = kb8 + C::TILE * 2 + vbase;          // ... and V reads
+    auto kread = [&](int kb, int kk) {
+      return *reinterpret_cast<const bf16x8*>(kl[kk & 1] + seg_rowop_imm<D>(kb, kk));
+    };
+    if (j + 1 < j1) load_tile(j + 1, jb ^ 1);
 
     // S^T = K_j Q^T in 32-key blocks; A = K rows from LDS (each read feeds
     // the QB query blocks), B = Q^T.  The K operands are read kReadAhead
@@ -140,7 +162,7 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < RA; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) kop[kk][kb] = rowop_read<D>(kl, kb, kk);
+      for (int kb = 0; kb < C::KB; ++kb) kop[kk][kb] = kread(kb, kk);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
       if (kk + RA < C::DK) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
-          kop[(kk + RA) % (RA + 1)][kb] = rowop_read<D>(kl, kb, kk + RA);
+          kop[(kk + RA) % (RA + 1)][kb] = kread(kb, kk + RA);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -229,12 +251,12 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
       constexpr int SA = kStepAhead, NS = (BC / 16) * C::DB;
       bf16x8 vop[SA + 1];
 #pragma unroll
-      for (int n = 0; n < SA; ++n) vop[n] = trop_read<D>(vl, n / C::DB, n % C::DB);
+      for (int n = 0; n < SA; ++n) vop[n] = seg_trop_read<D>(vl, n / C::DB, n % C::DB);
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         if (n + SA < NS) {
           const int m = n + SA;
-          vop[m % (SA + 1)] = trop_read<D>(vl, m / C::DB, m % C::DB);
+          vop[m % (SA + 1)] = seg_trop_read<D>(vl, m / C::DB, m % C::DB);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int t = n / C::DB, db = n % C::DB;

@@ -193,67 +193,61 @@ __device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p
 }
 
 // ---------------------------------------------------------------------------
-// Operand-ordered tiles.  When a tile is only ever read one way, it can be
-// stored in the order the reads consume it: every read is then one base
-// register plus an immediate offset (no per-read address arithmetic), and
-// consecutive lanes read consecutive bytes (no bank conflicts).  R rows of D
-// bf16 values.
-//
-// Row-operand order: block (kb, kk) (kb < R/32, kk < D/16), 1 KB, holds for
-// lane L the 8 values K[kb*32 + L%32][(2 kk + L/32) * 8 ..] at byte 16 L,
-// i.e. exactly a matrix-core A/B operand.  One direct load per block.
-template <int D, int R, int NW>
-__device__ __forceinline__ void rowop_load(uint16_t* tile, rsrc_t src, int r0, int wave,
-                                           int lane) {
-  constexpr int DK = D / 16, NB = (R / 32) * DK;
-  static_assert(NB % NW == 0, "the same number of instructions for every wave");
-#pragma unroll
-  for (int u = 0; u < NB / NW; ++u) {
-    const int b = wave + u * NW, kb = b / DK, kk = b % DK;
-    const int row = kb * 32 + (lane & 31), col = (2 * kk + (lane >> 5)) * 8;
-    lds_dma16(src, (uint32_t)((row * D + col) * 2),
-              __builtin_amdgcn_readfirstlane(lds_addr(tile + b * 512)),
-              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
-  }
+// Row-segment tiles.  R rows of D bf16 values in 1 KB blocks of 16 rows x 32
+// values: block (r16, c32) sits at byte (r16 * D/32 + c32) * 1024 and holds
+// the 64 bytes of its row rho at byte 64 rho, as four 16-byte pieces.  One
+// direct load fills one block, lanes 4 rho .. 4 rho + 3 reading the 64
+// contiguous source bytes of row rho: the load path runs at full rate only
+// when every four consecutive lanes read one contiguous 64-byte segment
+// (lanes spread over more rows, as in the operand orders above, run at a
+// half or a quarter of it).  With SWZ, piece p of row rho sits at position
+// p ^ ((rho >> 2) & 3), which keeps the row-operand reads conflict-free.
+template <int D, int NW, bool SWZ>
+__device__ __forceinline__ uint32_t seg_dma_voff(int wave, int lane) {
+  constexpr int C32 = D / 32;
+  static_assert(NW % C32 == 0, "whole 16-row steps between a wave's instructions");
+  const int rho = lane >> 2, pos = lane & 3;
+  const int p = SWZ ? pos ^ ((rho >> 2) & 3) : pos;
+  const int row = (wave / C32) * 16 + rho, col = (wave % C32) * 32 + p * 8;
+  return (uint32_t)((row * D + col) * 2);
 }
-// The operand of block (kb, kk) for this lane: `lanebase` = tile + 8 * lane.
+// Instruction u of wave `wave` fills block wave + u NW of the tile at LDS
+// byte address `tile_lds`; `row0_bytes` is the source offset of its row 0.
+template <int D, int NW>
+__device__ __forceinline__ void seg_dma(uint32_t tile_lds, rsrc_t src, uint32_t voff,
+                                        uint32_t row0_bytes, int wave, int u) {
+  constexpr int USTEP = (NW / (D / 32)) * 16 * D * 2;
+  lds_dma16(src, voff, tile_lds + (uint32_t)((wave + u * NW) * 1024),
+            row0_bytes + (uint32_t)(u * USTEP));
+}
+// Row operand of a swizzled row-segment tile: for 32-row block kb and k-step
+// kk, lane L takes the 8 values of row 32 kb + L % 32 at columns
+// 16 kk + 8 (L / 32) ..+7.  Byte offset of this lane's read for the k-steps
+// of parity e; the read of (kb, kk) is at that plus seg_rowop_imm(kb, kk).
 template <int D>
-__device__ __forceinline__ bf16x8 rowop_read(const uint16_t* lanebase, int kb, int kk) {
-  return lds_bf16x8(lanebase + (kb * (D / 16) + kk) * 512);
+__device__ __forceinline__ uint32_t seg_rowop_base(int lane, int e) {
+  const int rho = lane & 15, hb = (lane >> 4) & 1, g = lane >> 5;
+  return (uint32_t)(hb * (D / 32) * 1024 + 64 * rho + 16 * ((2 * e + g) ^ ((rho >> 2) & 3)));
 }
-
-// Transposing-read order: for 16-row step t (< R/16), 32-column block cb
-// (< D/32) and half h (0, 1), a 512-byte block holds at byte 8 s the source
-// lane s = 16 q + 4 a + b of a ds_read_b64_tr_b16: values
-// M[16 t + 8 h + 4 (q >> 1) + a][32 cb + 16 (q & 1) + 4 b ..+3].  The two
-// halves of (t, cb) are adjacent, and the 16 bytes a direct-load lane writes
-// (slots 2L, 2L + 1 of a 1 KB pair) are 8 consecutive values of one row.
-template <int D, int R, int NW>
-__device__ __forceinline__ void trop_load(uint16_t* tile, rsrc_t src, int r0, int wave,
-                                          int lane) {
-  constexpr int DB = D / 32, NP = (R / 16) * DB;    // 1 KB block pairs
-  static_assert(NP % NW == 0, "the same number of instructions for every wave");
-  const int h = lane >> 5, s = 2 * (lane & 31);
-  const int q = s >> 4, a = (s >> 2) & 3, b = s & 3;
-#pragma unroll
-  for (int u = 0; u < NP / NW; ++u) {
-    const int pidx = wave + u * NW, t = pidx / DB, cb = pidx % DB;
-    const int row = 16 * t + 8 * h + 4 * (q >> 1) + a;
-    const int col = 32 * cb + 16 * (q & 1) + 4 * b;
-    lds_dma16(src, (uint32_t)((row * D + col) * 2),
-              __builtin_amdgcn_readfirstlane(lds_addr(tile + pidx * 512)),
-              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
-  }
-}
-// Transposed operand (same values and order as tr_operand) of step t, block
-// cb for this lane: `lanebase` = tile + 4 * lane.
 template <int D>
-__device__ __forceinline__ bf16x8 trop_read(const uint16_t* lanebase, int t, int cb) {
-  const uint16_t* p = lanebase + (t * (D / 32) + cb) * 512;
+__host__ __device__ constexpr int seg_rowop_imm(int kb, int kk) {
+  return (2 * kb * (D / 32) + kk / 2) * 1024;
+}
+// Transposed operand (the values and order of tr_operand) of 16-row step t
+// and 32-column block cb of an unswizzled row-segment tile: this lane's
+// source rows 4 (q >> 1) + a and 8 more, columns 16 (q & 1) + 4 b ..+3.
+template <int D>
+__device__ __forceinline__ uint32_t seg_trop_base(int lane) {
+  const int i16 = lane & 15, q = lane >> 4, a = i16 >> 2, b = i16 & 3;
+  return (uint32_t)(64 * (4 * (q >> 1) + a) + 2 * (16 * (q & 1) + 4 * b));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 seg_trop_read(const uint8_t* lanebase, int t, int cb) {
+  const uint8_t* p = lanebase + (t * (D / 32) + cb) * 1024;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p + 256));
+      (__attribute__((address_space(3))) s16x4*)(p + 512));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
   return as_bf16x8(w);
