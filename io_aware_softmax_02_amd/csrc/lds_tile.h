@@ -199,8 +199,8 @@ __device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p
 // direct load fills one block, lanes 4 rho .. 4 rho + 3 reading the 64
 // contiguous source bytes of row rho: the load path runs at full rate only
 // when every four consecutive lanes read one contiguous 64-byte segment
-// (lanes spread over more rows, as in the operand orders above, run at a
-// half or a quarter of it).  With SWZ, piece p of row rho sits at position
+// (a load whose lanes cover 32 rows x 32 bytes, the order of a matrix-core
+// operand, runs at a quarter of it; two lanes per row at a half).  With SWZ, piece p of row rho sits at position
 // p ^ ((rho >> 2) & 3), which keeps the row-operand reads conflict-free.
 template <int D, int NW, bool SWZ>
 __device__ __forceinline__ uint32_t seg_dma_voff(int wave, int lane) {
