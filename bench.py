@@ -64,6 +64,9 @@ def parse():
                     help="fp32 path measurement instead of the headline one")
     ap.add_argument("--contrast", action="store_true",
                     help="materialised standard attention beside fa_fwd instead of the headline")
+    ap.add_argument("--configs", action="store_true",
+                    help="forward and fwd+bwd throughput on every named workload instead of "
+                         "the headline")
     return ap.parse_args()
 
 
@@ -177,6 +180,47 @@ def sweep(args):
             "fp32_scores_per_head_bytes": int(N * N * 4),
         }), flush=True)
         del q, k, v, dO, o, lse, dq, dk, dv, ws
+
+
+def configs(args):
+    """Forward and forward+backward throughput on each named workload (the
+    test and parity shapes, synth.WORKLOADS), one JSON line each.  The fp32
+    workload runs the fp32 entry points; the others the bf16 ones."""
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    for name, w in synth.WORKLOADS.items():
+        q, k, v, dO = (x.to(dev) for x in synth.make_inputs(w, backward=True))
+        f32 = w.dtype == "f32"
+        fwd_fn, bwd_fn = (fa.fa_fwd_f32, fa.fa_bwd_f32) if f32 else (fa.fa_fwd, fa.fa_bwd)
+        ws_bytes = (fa.fa_bwd_f32_workspace_bytes if f32 else fa.fa_bwd_workspace_bytes)(
+            w.B, w.H, w.N, w.d)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        fwd = lambda: fwd_fn(q, k, v, w.scale, o=o, lse=lse)
+        bwd = lambda: bwd_fn(q, k, v, o, lse, dO, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        fwd(); bwd()
+        torch.cuda.synchronize()
+        # about 50 ms of work per timed run, at least one launch
+        est = median_time(lambda: (fwd(), bwd()), 1, stream, 1)
+        inner = max(1, min(200, int(50.0 / max(est, 1e-3))))
+        med_f = median_time(fwd, inner, stream)
+        med_b = median_time(bwd, inner, stream)
+        fl_f, fl_b = w.fwd_flops(), w.bwd_flops()
+        print(json.dumps({
+            "workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
+            "launches": inner, "ms_fwd": round(med_f, 4), "ms_bwd": round(med_b, 4),
+            "fwd_tflops": round(fl_f / (med_f * 1e-3) / 1e12, 2),
+            "fwdbwd_tflops": round((fl_f + fl_b) / ((med_f + med_b) * 1e-3) / 1e12, 2),
+            "peak_tflops": PEAK_FP32_TFLOPS if f32 else PEAK_BF16_TFLOPS,
+        }), flush=True)
+        del q, k, v, dO, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
 
 
 def splitkv(args):
@@ -353,6 +397,8 @@ def main():
         return splitkv(args)
     if args.contrast:
         return contrast(args)
+    if args.configs:
+        return configs(args)
     if args.fp32:
         return fp32(args)
 

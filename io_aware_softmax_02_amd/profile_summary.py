@@ -17,6 +17,8 @@ leaves in its output directory into the short text summaries that are kept:
       the JSON lines of `bench.py --fp32` as markdown
   python -m io_aware_softmax_02_amd.profile_summary contrast LOG
       the JSON lines of `bench.py --contrast` as markdown
+  python -m io_aware_softmax_02_amd.profile_summary configs LOG
+      the JSON lines of `bench.py --configs` as markdown
   python -m io_aware_softmax_02_amd.profile_summary sweep LOG
   python -m io_aware_softmax_02_amd.profile_summary splitkv LOG
       the JSON lines of `bench.py --sweep` / `bench.py --splitkv` as markdown
@@ -217,6 +219,22 @@ def sweep_md(path: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def configs_md(path: str) -> str:
+    out = ["# Throughput on every named workload\n",
+           "Command (repository root, one MI355X): `python bench.py --configs > LOG; "
+           "python -m io_aware_softmax_02_amd.profile_summary configs LOG`\n",
+           "Times are the median of five runs of back-to-back launches (HIP events on the launch "
+           "stream). Counted work: forward 4·B·H·N²·d, backward 2.5× that. `% peak` is fwd+bwd "
+           "against the published dense peak of the dtype (bf16 2500, fp32 157.3 TF/s).\n",
+           "| workload | B, H, N, d | dtype | fwd µs | fwd TF/s | bwd µs | fwd+bwd TF/s | % peak |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in _json_lines(path):
+        out.append(f"| `{r['workload']}` | {r['B']}, {r['H']}, {r['N']}, {r['d']} | {r['dtype']} | "
+                   f"{r['ms_fwd'] * 1e3:.1f} | {r['fwd_tflops']} | {r['ms_bwd'] * 1e3:.1f} | "
+                   f"{r['fwdbwd_tflops']} | {100 * r['fwdbwd_tflops'] / r['peak_tflops']:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def splitkv_md(path: str) -> str:
     out = ["# Split-KV forward + merge against the plain forward (bf16, d = 128)\n",
            "Command (repository root, one MI355X): `python bench.py --splitkv > LOG; "
@@ -252,6 +270,8 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(fp32_md(argv[2]))
     elif cmd == "contrast":
         sys.stdout.write(contrast_md(argv[2]))
+    elif cmd == "configs":
+        sys.stdout.write(configs_md(argv[2]))
     elif cmd == "sweep":
         sys.stdout.write(sweep_md(argv[2]))
     elif cmd == "splitkv":
