@@ -471,6 +471,18 @@ def main():
     ms_dq = time_launches(lambda: fa.fa_bwd_dq(q, k, v, lse, dO, delta, s, dq=dq), n, stream)
     ms_bwd = time_launches(bwd, n, stream)
 
+    # Same-box reference for the matrix-core rate attainable on this kind of
+    # data (outside the timed region): one 8192^3 bf16 GEMM through torch
+    # (the vendor BLAS) on seeded N(0,1) operands.
+    gen = torch.Generator(device=dev).manual_seed(7)
+    ga = torch.randn(8192, 8192, generator=gen, device=dev).to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, generator=gen, device=dev).to(torch.bfloat16)
+    gc = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    torch.matmul(ga, gb, out=gc)
+    ms_gemm = median_time(lambda: torch.matmul(ga, gb, out=gc), 5, stream, 3)
+    gemm_tf = 2.0 * 8192 ** 3 / (ms_gemm * 1e-3) / 1e12
+    del ga, gb, gc, gen
+
     pairs = B * H * N * N
     f_fwd = w.fwd_flops()
     f_bwd = w.bwd_flops()
@@ -518,6 +530,10 @@ def main():
         "kernels": {kname: {"ms": round(kv["ms"], 4), "tflops": round(kv["tflops"], 2)}
                     for kname, kv in kernels.items()},
         "hbm_copy_GBps": round(2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9, 1),
+        "reference_gemm": {"what": "torch.matmul bf16 8192x8192x8192, N(0,1) operands",
+                           "tflops": round(gemm_tf, 1),
+                           "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+                           "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count},
         "peak_mem_bytes": int(peak_mem),
         "mem_inputs_outputs_bytes": int(mem_base),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
