@@ -331,10 +331,11 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   const auto* v16 = static_cast<const uint16_t*>(v);
   auto* o16 = static_cast<uint16_t*>(o);
   // d = 128: 8 waves x 32 query rows, key tiles of 128 (one workgroup per CU,
-  // two waves per SIMD); d = 64: 4 waves x 32 rows, key tiles of 64.
+  // two waves per SIMD); d = 64: 8 waves x 32 rows, key tiles of 64 (two
+  // workgroups per CU).
   if (d == 128)
     return launch<128, 1, 128, 2, true, 8>(q16, k16, v16, o16, lse, BH, N, scale, 1, stream);
-  return launch<64, 1, 64, 2, false, 4>(q16, k16, v16, o16, lse, BH, N, scale, 1, stream);
+  return launch<64, 1, 64, 2, false, 8>(q16, k16, v16, o16, lse, BH, N, scale, 1, stream);
 }
 
 int fwd_split_tile(int64_t d) { return d == 128 ? 128 : 64; }
@@ -348,7 +349,7 @@ int launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* o_
   if (d == 128)
     return launch<128, 1, 128, 2, true, 8, true>(q16, k16, v16, o_part, lse_part, BH, N, scale,
                                                  nsplit, stream);
-  return launch<64, 1, 64, 2, false, 4, true>(q16, k16, v16, o_part, lse_part, BH, N, scale,
+  return launch<64, 1, 64, 2, false, 8, true>(q16, k16, v16, o_part, lse_part, BH, N, scale,
                                               nsplit, stream);
 }
 
