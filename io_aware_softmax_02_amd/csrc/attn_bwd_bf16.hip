@@ -423,7 +423,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup owns 128 queries (4 waves x 32), loops over 64-key tiles.
+// dQ: workgroup owns 256 queries (8 waves x 32, two per SIMD), loops over
+// 64-key tiles; each K/V tile in LDS serves all 256 queries.
 // Per wave and tile (lane l: query l%32 of the wave's block):
 //   S^T  = K Q^T    (A = K rows from LDS, B = Q regs)
 //   dP^T = V dO^T   (A = V rows from LDS, B = dO regs)
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-  static constexpr int BQ = 128, BK = 64, WAVES = 4, THREADS = 64 * WAVES;
+  static constexpr int BQ = 256, BK = 64, WAVES = 8, THREADS = 64 * WAVES;
   static constexpr int TILE = BK * D;          // one K or V tile (bf16), swizzled
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = TILE;
@@ -444,7 +445,7 @@ struct DqCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(512, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta,
