@@ -34,7 +34,7 @@ namespace {
 constexpr int kReadAhead = 2;
 constexpr int kStepAhead = 4;
 constexpr int kDkdvStepAhead = 4;
-constexpr int kDkdvReadAhead = 3;
+constexpr int kDkdvReadAhead = 2;
 
 // ---------------------------------------------------------------------------
 // Preprocess: D_i = sum_c dO_ic O_ic (fp32).  D/8 lanes per row, 16 B each.
