@@ -228,6 +228,25 @@ def test_bf16_ragged_forward_backward(N, d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(3, 1, 255), (1, 3, 257), (1, 1, 4097)])
+def test_bf16_ragged_at_workgroup_boundaries(B, H, N, d):
+    """One row short of and past 256 (the query rows of a forward or dQ
+    workgroup, two 128-key dK/dV tiles), and a long ragged tail; grids whose
+    sizes are not multiples of the 8 XCDs."""
+    say(f"case bf16 boundary B={B} H={H} N={N} d={d}")
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=400 + N + d, backward=True)
+    s = synth.default_scale(d)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, s)
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
+    check_fwd_bf16(O, L, Oref, Lref, f"  fwd B={B} H={H} N={N} d={d}")
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = grad_err(f64(x), ref)
+        say(f"  {name} err {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_bf16_q_zero(d):
     """Q = 0: O is the column mean of V, LSE = ln N, dK is exactly zero and
     every dV row is the mean of dO's rows."""
