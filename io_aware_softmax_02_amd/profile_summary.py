@@ -131,12 +131,13 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
                    "512 MiB device copy run in the same bench process",
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": cf,
                            "write_size_kib": cw, "read_factor": rf, "write_factor": wf},
+           # the output directories are the ones the two CSVs were read from
            "commands": [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} --kernel-include-regex '{rx}' "
-                        f"-f csv -d gpurun_out/pmc_{t} -o pmc -- python3 bench.py --steps 2 "
-                        f"--warmup 1 --no-cpu-baseline" for c, t in (("FETCH_SIZE", "F"), ("WRITE_SIZE", "W"))]
-                       + ["python -m io_aware_softmax_02_amd.profile_summary traffic "
-                          "gpurun_out/pmc_F/pmc_counter_collection.csv "
-                          "gpurun_out/pmc_W/pmc_counter_collection.csv " + out_json],
+                        f"-f csv -d {os.path.dirname(csv)} -o pmc -- python3 bench.py --steps 2 "
+                        f"--warmup 1 --no-cpu-baseline"
+                        for c, csv in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
+                       + [f"python -m io_aware_softmax_02_amd.profile_summary traffic "
+                          f"{fetch_csv} {write_csv} {out_json}"],
            "kernels": kern}
     with open(out_json, "w") as fh:
         json.dump(doc, fh, indent=1)
