@@ -102,11 +102,14 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[qb][db] = zero16();
-  float m_run[QB], l_run[QB];   // reference value (log2 units) and this lane's share of l
+  // Reference value (log2 units) and this lane's share of l; lb is the same
+  // sum taken over the bf16-rounded P~ that the PV contraction multiplies.
+  float m_run[QB], l_run[QB], lb_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.0f;
+    lb_run[qb] = 0.0f;
   }
 
   // Key tiles [j0, j1): all of them, or this workgroup's range in split mode
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
         const float m_new = fmaxf(m_run[qb], m_cand);
         const float alpha = fast_exp2(m_run[qb] - m_new);   // 0 on the first tile
         l_run[qb] *= alpha;
+        lb_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
       // P~ in fp32 for the row sum, rounded to bf16 (RNE) in the B-operand
       // layout of the next contraction: elements 8h..8h+7 of score block kb
       // hold the keys of 16-key step t = 2 kb + h in the operand's k order.
-      float rs = 0.0f;
+      float rs = 0.0f, rb0 = 0.0f, rb1 = 0.0f;
 #pragma unroll
       for (int t = 0; t < BC / 16; ++t) {
         const int kb = t >> 1, h = t & 1;
@@ -236,10 +240,13 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
           const float p1 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e + 1], c2, -m_run[qb]));
           rs += p0 + p1;
           pw[e] = pack_bf16x2(p0, p1);
+          if (e & 1) rb1 = add_bf16x2(pw[e], rb1);
+          else rb0 = add_bf16x2(pw[e], rb0);
         }
         pb[qb][t] = as_bf16x8(pw);
       }
       l_run[qb] += rs;
+      lb_run[qb] += rb0 + rb1;
     }
 
     // O^T += V_j^T P^T over steps n = (t, db): 16-key step t, 32-column
@@ -274,9 +281,13 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = qrow0 + 32 * qb;
+    // O is divided by the sum of the rounded weights it was accumulated
+    // with, so it is a convex combination of V rows whatever the rounding
+    // (a dominant key's rounding cancels); the LSE uses the fp32 sum.
     const float l_tot = sum_across_halves(l_run[qb]);
+    const float lb_tot = sum_across_halves(lb_run[qb]);
     if (qrow < N) {
-      const float inv = 1.0f / l_tot;
+      const float inv = 1.0f / lb_tot;
       if (SPLIT) {   // fp32 output of this key range, at part p of the partial tensors
         float* orow = static_cast<float*>(o) + part * part_rows * D + hoff + (int64_t)qrow * D;
 #pragma unroll

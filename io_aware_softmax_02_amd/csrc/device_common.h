@@ -114,6 +114,14 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 // Lanes l and l ^ 32 exchange a value with v_permlane32_swap: called with
 // the same register twice, the two results hold x[l % 32] and x[l % 32 + 32]
 // in every lane (a VALU op, no LDS round trip).
+// acc + a.lo + a.hi for the two bf16 values packed in the dword a (one
+// v_dot2 against (1, 1); the products are exact).
+__device__ __forceinline__ float add_bf16x2(uint32_t a, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
 __device__ __forceinline__ float max_across_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);

@@ -112,6 +112,28 @@ def test_f32_backward(B, H, N, d):
         assert e <= TOL_F32_GRAD_REL, name
 
 
+# The scale enters the exponent factor, the statistics and the dQ/dK scaling;
+# every other test uses 1/sqrt(d).  0.25 at d = 128 makes rows peaky.
+@pytest.mark.parametrize("d", [24, 128])
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_f32_nondefault_scale(d, scale):
+    say(f"case f32 scale={scale} d={d}")
+    s = float(np.float32(scale))
+    q, k, v, dO = synth.make_qkv(1, 2, 300, d, torch.float32, seed=500 + d, backward=True)
+    qg, kg, vg, gg = gpu(q), gpu(k), gpu(v), gpu(dO)
+    O, L = fa.fa_fwd_f32(qg, kg, vg, s)
+    dq, dk, dv = fa.fa_bwd_f32(qg, kg, vg, O, L, gg, s)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
+    assert max_abs(f64(O), Oref) <= TOL_F32
+    assert max_abs(f64(L), Lref) <= TOL_F32
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = grad_err(f64(x), ref)
+        say(f"  {name} rel-Frobenius {e:.2e}")
+        assert e <= TOL_F32_GRAD_REL, name
+
+
 # ---------------------------------------------------------------------------
 # bf16 path: workloads at full size
 # ---------------------------------------------------------------------------
@@ -239,6 +261,22 @@ def test_bf16_ragged_at_workgroup_boundaries(B, H, N, d):
     O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, s)
     Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
     check_fwd_bf16(O, L, Oref, Lref, f"  fwd B={B} H={H} N={N} d={d}")
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        e = grad_err(f64(x), ref)
+        say(f"  {name} err {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_bf16_nondefault_scale(d, scale):
+    say(f"case bf16 scale={scale} d={d}")
+    s = float(np.float32(scale))
+    q, k, v, dO = synth.make_qkv(1, 2, 777, d, torch.bfloat16, seed=600 + d, backward=True)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, s)
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), s)
+    check_fwd_bf16(O, L, Oref, Lref, f"  fwd scale={scale} d={d}")
     rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), s)
     for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
         e = grad_err(f64(x), ref)
