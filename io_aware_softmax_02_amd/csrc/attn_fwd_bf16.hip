@@ -43,6 +43,7 @@ namespace {
 
 // Slack of the lazily updated softmax reference, in log2 units.
 constexpr float kSlack = 8.0f;
+constexpr float kSlackPow = 256.0f;   // 2^kSlack
 // k-steps of K operands, and (t, db) steps of V^T operands, read from LDS
 // ahead of their use.
 constexpr int kReadAhead = 2;
@@ -205,18 +206,47 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     // P~ = 2^(c s - m_run) then stays <= 2^kSlack, and because U and l share
     // the same reference value the result O = U / l is unchanged (the
     // rescale identity holds for any common reference, not only the maximum).
+    // No row maximum is taken on the common path: the exponentials are
+    // formed against the current reference first, and their fp32 lane sum
+    // tells whether it has to move.
     bf16x8 pb[QB][BC / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
+      // Exponentials against the current reference, packed to bf16; rs is
+      // this lane's fp32 sum, rb the sum of the packed values.
+      float rs, rb;
+      auto exps = [&]() {
+        float r = 0.0f, b0 = 0.0f, b1 = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+        for (int t = 0; t < BC / 16; ++t) {
+          const int kb = t >> 1, h = t & 1;
+          u32x4 pw;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-      mx = max_across_halves(mx);
-      const float m_cand = mx * c2;
-      if (__any(m_cand > m_run[qb] + kSlack)) {
-        const float m_new = fmaxf(m_run[qb], m_cand);
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e], c2, -m_run[qb]));
+            const float p1 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e + 1], c2, -m_run[qb]));
+            r += p0 + p1;
+            pw[e] = pack_bf16x2(p0, p1);
+            if (e & 1) b1 = add_bf16x2(pw[e], b1);
+            else b0 = add_bf16x2(pw[e], b0);
+          }
+          pb[qb][t] = as_bf16x8(pw);
+        }
+        rs = r;
+        rb = b0 + b1;
+      };
+      exps();
+      // The reference must move when some P~ exceeds 2^kSlack; a lane sum
+      // above that (or not a number: first tile, m_run = -inf) is necessary
+      // for it, and only then is the row maximum taken.
+      if (__any(!(rs <= kSlackPow))) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+        mx = max_across_halves(mx);
+        const float m_new = fmaxf(m_run[qb], mx * c2);
         const float alpha = fast_exp2(m_run[qb] - m_new);   // 0 on the first tile
         l_run[qb] *= alpha;
         lb_run[qb] *= alpha;
@@ -225,28 +255,10 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
         m_run[qb] = m_new;
-      }
-      // P~ in fp32 for the row sum, rounded to bf16 (RNE) in the B-operand
-      // layout of the next contraction: elements 8h..8h+7 of score block kb
-      // hold the keys of 16-key step t = 2 kb + h in the operand's k order.
-      float rs = 0.0f, rb0 = 0.0f, rb1 = 0.0f;
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t) {
-        const int kb = t >> 1, h = t & 1;
-        u32x4 pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e], c2, -m_run[qb]));
-          const float p1 = fast_exp2(fmaf(s[qb][kb][8 * h + 2 * e + 1], c2, -m_run[qb]));
-          rs += p0 + p1;
-          pw[e] = pack_bf16x2(p0, p1);
-          if (e & 1) rb1 = add_bf16x2(pw[e], rb1);
-          else rb0 = add_bf16x2(pw[e], rb0);
-        }
-        pb[qb][t] = as_bf16x8(pw);
+        exps();
       }
       l_run[qb] += rs;
-      lb_run[qb] += rb0 + rb1;
+      lb_run[qb] += rb;
     }
 
     // O^T += V_j^T P^T over steps n = (t, db): 16-key step t, 32-column
