@@ -9,19 +9,23 @@
 //   U are updated with the rescale factor 2^(m_old - m_new) (the identity
 //   e^{x-m_new} = e^{x-m_old} e^{m_old-m_new} of the star-observatory fable,
 //   section "兩大核心魔法"), and at the end O = U / l and LSE = m + ln l are
-//   the only values written back (算珠楼的掌簿人, 技术解读).
+//   the only values written back (算珠楼的掌簿人, 技术解读).  Two sums are
+//   kept: l in fp32 for the LSE, and the sum of the bf16-rounded weights U
+//   was accumulated with, which O is divided by (so O is a convex
+//   combination of V rows in the arithmetic performed).
 //
 // Work decomposition:
 //   workgroup = NWAVES waves; each wave owns QB blocks of 32 query rows of one
 //   (batch, head).  Key tiles of BC rows stream through LDS, double-buffered:
 //   direct buffer->LDS loads of tile j+1 are issued at the start of tile j
 //   (no registers involved), one barrier per tile.  With QB = 2 every K and V
-//   operand read from LDS feeds two matrix-core instructions, halving LDS
-//   traffic per flop.
+//   operand read from LDS would feed two matrix-core instructions; the
+//   instantiations below use QB = 1 and more waves, which measured faster.
 //   Scores are formed transposed, S^T = K Q^T, so that each lane owns one
 //   query row: lane l holds query l%32 for 16 of every 32 keys (the other 16
-//   sit in lane l^32).  The row max and row sum are in-lane reductions plus
-//   one exchange between the two half-waves.  The probabilities leave the
+//   sit in lane l^32).  Row sums are in-lane; the row max, taken only when
+//   the softmax reference has to move, is an in-lane reduction plus one
+//   exchange between the two half-waves.  The probabilities leave the
 //   score accumulators already in the B-operand layout of O^T += V^T P^T, so
 //   P never touches LDS; the V^T operand is gathered from the V tile with
 //   transposing LDS reads in the matching key order.  Both tiles are stored
