@@ -91,15 +91,15 @@ def median_time(fn, inner, stream, outer=5):
 
 def measured_traffic(kernel):
     """Calibrated HBM bytes per launch of `kernel`, or None if not measured
-    for the current sources."""
-    import hashlib
+    for the current sources (digests of their code, comments excluded)."""
+    from io_aware_softmax_02_amd.profile_summary import code_digest
     try:
         rec = json.load(open(TRAFFIC_FILE))["kernels"][kernel]
     except (OSError, KeyError, ValueError):
         return None
     for rel, digest in rec["source_sha256"].items():
         try:
-            cur = hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()
+            cur = code_digest(os.path.join(ROOT, rel))
         except OSError:
             return None
         if cur != digest:

@@ -53,9 +53,20 @@ def short(name: str) -> str:
     return re.sub(r"\(.*", "", name)
 
 
+def code_digest(path: str) -> str:
+    """sha256 of a source file with its // and /* */ comments and all
+    whitespace removed: a measurement stays valid across comment edits but
+    not across code changes.  (Comment markers inside string literals would
+    be stripped too; the kernel sources have none that matter.)"""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()
+
+
 def source_digests() -> dict:
-    return {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
-            for p in TRAFFIC_SOURCES}
+    return {p: code_digest(os.path.join(ROOT, p)) for p in TRAFFIC_SOURCES}
 
 
 def trace(db_glob: str, title: str, cmd: str) -> str:
