@@ -200,14 +200,20 @@ __device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p
 // contiguous source bytes of row rho: the load path runs at full rate only
 // when every four consecutive lanes read one contiguous 64-byte segment
 // (a load whose lanes cover 32 rows x 32 bytes, the order of a matrix-core
-// operand, runs at a quarter of it; two lanes per row at a half).  With SWZ, piece p of row rho sits at position
-// p ^ ((rho >> 2) & 3), which keeps the row-operand reads conflict-free.
-template <int D, int NW, bool SWZ>
+// operand, runs at a quarter of it; two lanes per row at a half).  Piece p
+// of row rho sits at position p ^ seg_swz<SWZ>(rho): kind 1 keeps the
+// row-operand reads free of bank conflicts, kind 2 the 16 x 16 transposing
+// reads (below), kind 0 is no swizzle.
+template <int SWZ>
+__host__ __device__ constexpr int seg_swz(int rho) {
+  return SWZ == 1 ? ((rho >> 2) & 3) : SWZ == 2 ? 2 * ((rho >> 2) & 1) : 0;
+}
+template <int D, int NW, int SWZ>
 __device__ __forceinline__ uint32_t seg_dma_voff(int wave, int lane) {
   constexpr int C32 = D / 32;
   static_assert(NW % C32 == 0, "whole 16-row steps between a wave's instructions");
   const int rho = lane >> 2, pos = lane & 3;
-  const int p = SWZ ? pos ^ ((rho >> 2) & 3) : pos;
+  const int p = pos ^ seg_swz<SWZ>(rho);
   const int row = (wave / C32) * 16 + rho, col = (wave % C32) * 32 + p * 8;
   return (uint32_t)((row * D + col) * 2);
 }
@@ -220,34 +226,38 @@ __device__ __forceinline__ void seg_dma(uint32_t tile_lds, rsrc_t src, uint32_t 
   lds_dma16(src, voff, tile_lds + (uint32_t)((wave + u * NW) * 1024),
             row0_bytes + (uint32_t)(u * USTEP));
 }
-// Row operand of a swizzled row-segment tile: for 32-row block kb and k-step
-// kk, lane L takes the 8 values of row 32 kb + L % 32 at columns
-// 16 kk + 8 (L / 32) ..+7.  Byte offset of this lane's read for the k-steps
-// of parity e; the read of (kb, kk) is at that plus seg_rowop_imm(kb, kk).
-template <int D>
-__device__ __forceinline__ uint32_t seg_rowop_base(int lane, int e) {
-  const int rho = lane & 15, hb = (lane >> 4) & 1, g = lane >> 5;
-  return (uint32_t)(hb * (D / 32) * 1024 + 64 * rho + 16 * ((2 * e + g) ^ ((rho >> 2) & 3)));
+// Operands of the 16 x 16 x 32 instruction (device_common.h).
+// Row operand from a kind-1 tile: for 16-row block kb and 32-column k-step
+// kk, lane L takes the 8 values of row 16 kb + L % 16 at columns
+// 32 kk + 8 (L / 16) ..+7.  The 16 lanes of one k-group read 16 rows of one
+// logical piece, which the swizzle spreads over all 64 banks.
+__device__ __forceinline__ uint32_t seg_rowop16_base(int lane) {
+  const int rho = lane & 15, g = lane >> 4;
+  return (uint32_t)(64 * rho + 16 * (g ^ seg_swz<1>(rho)));
 }
 template <int D>
-__host__ __device__ constexpr int seg_rowop_imm(int kb, int kk) {
-  return (2 * kb * (D / 32) + kk / 2) * 1024;
+__host__ __device__ constexpr int seg_rowop16_imm(int kb, int kk) {
+  return (kb * (D / 32) + kk) * 1024;
 }
-// Transposed operand (the values and order of tr_operand) of 16-row step t
-// and 32-column block cb of an unswizzled row-segment tile: this lane's
-// source rows 4 (q >> 1) + a and 8 more, columns 16 (q & 1) + 4 b ..+3.
-template <int D>
-__device__ __forceinline__ uint32_t seg_trop_base(int lane) {
-  const int i16 = lane & 15, q = lane >> 4, a = i16 >> 2, b = i16 & 3;
-  return (uint32_t)(64 * (4 * (q >> 1) + a) + 2 * (16 * (q & 1) + 4 * b));
+// Transposed operand from a kind-2 tile: for 32-row step t and 16-column
+// block cb, lane L (column 16 cb + L % 16, k-group g = L / 16) takes rows
+// 32 t + 4 g + 0..3 (elements 0..3) and 32 t + 16 + 4 g + 0..3 (elements
+// 4..7) of its column: the key order of two 16 x 16 score accumulators of
+// 16 keys each.  Source lane 4 a + b of group g addresses row 4 g + a of the
+// block, columns 16 (cb & 1) + 4 b ..+3; the swizzle puts the rows 4 apart
+// that one half-wave reads on different banks.  Base for blocks of parity e.
+__device__ __forceinline__ uint32_t seg_trop16_base(int lane, int e) {
+  const int i16 = lane & 15, g = lane >> 4, a = i16 >> 2, b = i16 & 3;
+  const int rho = 4 * g + a;
+  return (uint32_t)(64 * rho + 16 * ((2 * e + (b >> 1)) ^ seg_swz<2>(rho)) + 8 * (b & 1));
 }
 template <int D>
-__device__ __forceinline__ bf16x8 seg_trop_read(const uint8_t* lanebase, int t, int cb) {
-  const uint8_t* p = lanebase + (t * (D / 32) + cb) * 1024;
+__device__ __forceinline__ bf16x8 seg_trop16_read(const uint8_t* lanebase, int t, int cb) {
+  const uint8_t* p = lanebase + (2 * t * (D / 32) + cb / 2) * 1024;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p + 512));
+      (__attribute__((address_space(3))) s16x4*)(p + (D / 32) * 1024));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
   return as_bf16x8(w);

@@ -27,7 +27,7 @@ def test_code_digest_sees_every_kernel_source_change(tmp_path):
     p = tmp_path / "k.hip"
     p.write_text(text)
     d0 = code_digest(str(p))
-    p.write_text(text.replace("constexpr int kStepAhead = 4;", "constexpr int kStepAhead = 5;"))
+    p.write_text(text.replace("constexpr float kSlack = 8.0f;", "constexpr float kSlack = 7.0f;"))
     assert code_digest(str(p)) != d0
     p.write_text(text + "\n// trailing comment\n")
     assert code_digest(str(p)) == d0
