@@ -426,33 +426,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // dQ: workgroup owns 256 queries (8 waves x 32, two per SIMD), loops over
 // 64-key tiles; each K/V tile in LDS serves all 256 queries.  A wave raises
 // its priority while it issues matrix-core instructions, so that the other
-// wave of its SIMD runs its vector work in between (1.5% faster).
-// Per wave and tile (lane l: query l%32 of the wave's block):
+// wave of its SIMD runs its vector work in between.
+// The contractions use the 16 x 16 x 32 instruction (device_common.h): a
+// wave owns two 16-query blocks, and lane l holds query l%16 of each block
+// for keys 4(l/16) + 0..3 of every 16 keys.  Per wave and 32-key block:
 //   S^T  = K Q^T    (A = K rows from LDS, B = Q regs)
 //   dP^T = V dO^T   (A = V rows from LDS, B = dO regs)
-//   P^T = 2^(c S^T - LSE log2 e), dS^T = P^T (dP^T - D)   (lane-uniform stats)
+//   P^T = 2^(c S^T - LSE log2 e), dS^T = P^T (dP^T - D)   (per-query stats)
 //   dQ^T += K^T dS^T (A = K^T from LDS, B = dS^T from the accumulators)
-// Keys past N read as zero rows of K and V, so their dS multiplies a zero row
-// of K^T and adds nothing to dQ.
+// K and V tiles are in row-segment order (lds_tile.h): K is read along rows
+// for S^T and with transposing reads for K^T, so its swizzle (kind 3) serves
+// both; V is read along rows only (kind 1).  Keys past N read as zero rows
+// of K and V, so their dS multiplies a zero row of K^T and adds nothing to dQ.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
   static constexpr int BQ = 256, BK = 64, WAVES = 8, THREADS = 64 * WAVES;
-  static constexpr int TILE = BK * D;          // one K or V tile (bf16), swizzled
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = TILE;
-  static constexpr int BUF_ELEMS = 2 * TILE;
+  static constexpr int TILE = BK * D;          // one K or V tile (bf16)
+  static constexpr int BUF_ELEMS = 2 * TILE;   // K tile then V tile
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int DK = D / 16, DB = D / 32;
+  static constexpr int DK = D / 32, DB = D / 16;
 };
 
-template <int D>
-__global__ __launch_bounds__(512, 2) void bwd_dq_kernel(
+template <int D, int RA = kReadAhead, int SA = kStepAhead>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int N, int nqt, float c2, float scale) {
   using C = DqCfg<D>;
+  static_assert(RA <= 2 * C::DK && SA <= C::DB, "read-ahead within one block's operands");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -466,96 +469,128 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 31, g = lane >> 5;
-  const int qrow = qt * C::BQ + wave * 32 + li;
+  const int li = lane & 15, g = lane >> 4;
+  const int qrow0 = qt * C::BQ + wave * 32 + li;   // rows qrow0 and qrow0 + 16
 
-  bf16x8 qreg[C::DK], oreg[C::DK];
+  bf16x8 qreg[2][C::DK], oreg[2][C::DK];
+  float lse2[2], dl[2];
 #pragma unroll
-  for (int kk = 0; kk < C::DK; ++kk) {
-    const uint32_t off = (uint32_t)((qrow * D + kk * 16 + g * 8) * 2);
-    qreg[kk] = as_bf16x8(buf_load16(rq, off));
-    oreg[kk] = as_bf16x8(buf_load16(rdo, off));
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qrow0 + 16 * qb;
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) {
+      const uint32_t off = (uint32_t)((qrow * D + kk * 32 + g * 8) * 2);
+      qreg[qb][kk] = as_bf16x8(buf_load16(rq, off));
+      oreg[qb][kk] = as_bf16x8(buf_load16(rdo, off));
+    }
+    lse2[qb] = qrow < N ? lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
+    dl[qb] = qrow < N ? delta[(int64_t)bh * N + qrow] : 0.0f;
   }
-  const float lse2 = qrow < N ? lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dl = qrow < N ? delta[(int64_t)bh * N + qrow] : 0.0f;
 
-  f32x16 dqt[C::DB];
+  f32x4 dqt[2][C::DB];   // dQ^T blocks: lane l holds columns 16 db + 4 g + 0..3
 #pragma unroll
-  for (int cb = 0; cb < C::DB; ++cb) dqt[cb] = zero16();
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) dqt[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nkt = (N + C::BK - 1) / C::BK;
-  tile_load<D, C::BK, C::WAVES>(smem + C::OFF_K, rk, 0, wave, lane);
-  tile_load<D, C::BK, C::WAVES>(smem + C::OFF_V, rv, 0, wave, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t kvoff = seg_dma_voff<D, C::WAVES, 3>(wave, lane);
+  const uint32_t vvoff = seg_dma_voff<D, C::WAVES, 1>(wave, lane);
+  constexpr int NU = (C::BK / 16) * (D / 32) / C::WAVES;
+  static_assert(NU * C::WAVES == (C::BK / 16) * (D / 32), "whole loads per wave");
+  auto load_tile = [&](int jt, int b) {
+    uint32_t kd = lds0 + (uint32_t)(b * C::BUF_ELEMS * 2), vd = kd + (uint32_t)(C::TILE * 2);
+    const uint32_t r0 = (uint32_t)(jt * C::BK * D * 2);
+    asm volatile("" : "+s"(kd), "+s"(vd));   // one address per buffer, not one per load
+#pragma unroll
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, kvoff, r0, wave, u);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, vvoff, r0, wave, u);
+  };
+  const uint32_t krow = seg_rowop16_base<3>(lane), vrow = seg_rowop16_base<1>(lane);
+  const uint32_t ktr0 = seg_trop16_base<3>(lane, 0), ktr1 = seg_trop16_base<3>(lane, 1);
+  load_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < nkt; ++it) {
-    const uint16_t* buf = smem + (it & 1) * C::BUF_ELEMS;
-    const uint16_t* Ks = buf + C::OFF_K;
-    const uint16_t* Vs = buf + C::OFF_V;
-    if (it + 1 < nkt) {
-      uint16_t* nbuf = smem + ((it + 1) & 1) * C::BUF_ELEMS;
-      tile_load<D, C::BK, C::WAVES>(nbuf + C::OFF_K, rk, (it + 1) * C::BK, wave, lane);
-      tile_load<D, C::BK, C::WAVES>(nbuf + C::OFF_V, rv, (it + 1) * C::BK, wave, lane);
-    }
+    uint32_t bo = (uint32_t)((it & 1) * C::BUF_ELEMS * 2);
+    asm volatile("" : "+s"(bo));
+    const uint8_t* kt8 = reinterpret_cast<const uint8_t*>(smem) + bo;
+    const uint8_t* vt8 = kt8 + C::TILE * 2;
+    const uint8_t* ktr[2] = {kt8 + ktr0, kt8 + ktr1};
+    if (it + 1 < nkt) load_tile(it + 1, (it + 1) & 1);
 
-    // One 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (operands
-    // read kReadAhead k-steps ahead), then P^T and dS^T for this lane's
-    // query, then dQ^T += K^T dS^T for the block's two 16-key steps (K^T
-    // gathered with transposing reads kStepAhead steps ahead).  Only one
-    // block's scores are live at a time.
+    // One 32-key block at a time: S^T = K Q^T and dP^T = V dO^T over
+    // operands n = (k-step n / 2, 16-key half n % 2), then P^T and dS^T in
+    // the B-operand order of dQ^T += K^T dS^T, then that contraction with
+    // K^T gathered by transposing reads.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+    for (int kb2 = 0; kb2 < C::BK / 32; ++kb2) {
+      f32x4 s[2][2], dp[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          s[qb][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          dp[qb][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
       {
-        constexpr int RA = kReadAhead;
+        constexpr int NS = 2 * C::DK;
+        auto rd = [&](const uint8_t* base, int n) {
+          return *reinterpret_cast<const bf16x8*>(
+              base + seg_rowop16_imm<D>(2 * kb2 + n % 2, n / 2));
+        };
         bf16x8 ka[RA + 1], va[RA + 1];
 #pragma unroll
-        for (int kk = 0; kk < RA; ++kk) {
-          ka[kk] = row_operand<D>(Ks, kb * 32 + li, 2 * kk + g);
-          va[kk] = row_operand<D>(Vs, kb * 32 + li, 2 * kk + g);
+        for (int n = 0; n < RA; ++n) {
+          ka[n] = rd(kt8 + krow, n);
+          va[n] = rd(vt8 + vrow, n);
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) {
-          if (kk + RA < C::DK) {
-            ka[(kk + RA) % (RA + 1)] = row_operand<D>(Ks, kb * 32 + li, 2 * (kk + RA) + g);
-            va[(kk + RA) % (RA + 1)] = row_operand<D>(Vs, kb * 32 + li, 2 * (kk + RA) + g);
+        for (int n = 0; n < NS; ++n) {
+          if (n + RA < NS) {
+            ka[(n + RA) % (RA + 1)] = rd(kt8 + krow, n + RA);
+            va[(n + RA) % (RA + 1)] = rd(vt8 + vrow, n + RA);
           }
           __builtin_amdgcn_sched_barrier(0);
-          s = mfma32(ka[kk % (RA + 1)], qreg[kk], s);
-          dp = mfma32(va[kk % (RA + 1)], oreg[kk], dp);
+          const int kk = n / 2, h = n % 2;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            s[qb][h] = mfma16(ka[n % (RA + 1)], qreg[qb][kk], s[qb][h]);
+            dp[qb][h] = mfma16(va[n % (RA + 1)], oreg[qb][kk], dp[qb][h]);
+          }
         }
         __builtin_amdgcn_s_setprio(0);
       }
       bf16x8 sb[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int qb = 0; qb < 2; ++qb) {
         u32x4 sw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[8 * h + 2 * e], c2, -lse2));
-          const float p1 = fast_exp2(fmaf(s[8 * h + 2 * e + 1], c2, -lse2));
-          sw[e] = pack_bf16x2(p0 * (dp[8 * h + 2 * e] - dl), p1 * (dp[8 * h + 2 * e + 1] - dl));
+          const int h = e >> 1, i = 2 * (e & 1);
+          const float p0 = fast_exp2(fmaf(s[qb][h][i], c2, -lse2[qb]));
+          const float p1 = fast_exp2(fmaf(s[qb][h][i + 1], c2, -lse2[qb]));
+          sw[e] = pack_bf16x2(p0 * (dp[qb][h][i] - dl[qb]), p1 * (dp[qb][h][i + 1] - dl[qb]));
         }
-        sb[h] = as_bf16x8(sw);
+        sb[qb] = as_bf16x8(sw);
       }
       {
-        constexpr int SA = kStepAhead, NS = 2 * C::DB;   // steps n = (h, cb)
         bf16x8 ka[SA + 1];
 #pragma unroll
-        for (int n = 0; n < SA; ++n)
-          ka[n] = tr_operand<D>(Ks, (2 * kb + n / C::DB) * 16, (n % C::DB) * 32, lane);
+        for (int n = 0; n < SA; ++n) ka[n] = seg_trop16_read<D>(ktr[n & 1], kb2, n);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          if (n + SA < NS) {
-            const int m = n + SA;
-            ka[m % (SA + 1)] = tr_operand<D>(Ks, (2 * kb + m / C::DB) * 16, (m % C::DB) * 32, lane);
-          }
+        for (int db = 0; db < C::DB; ++db) {
+          if (db + SA < C::DB)
+            ka[(db + SA) % (SA + 1)] = seg_trop16_read<D>(ktr[(db + SA) & 1], kb2, db + SA);
           __builtin_amdgcn_sched_barrier(0);
-          const int cb = n % C::DB;
-          dqt[cb] = mfma32(ka[n % (SA + 1)], sb[n / C::DB], dqt[cb]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            dqt[qb][db] = mfma16(ka[db % (SA + 1)], sb[qb], dqt[qb][db]);
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -565,17 +600,19 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(
     __syncthreads();
   }
 
-  if (qrow < N) {
-    uint16_t* dqr = dq + hoff + (int64_t)qrow * D;
 #pragma unroll
-    for (int cb = 0; cb < C::DB; ++cb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qrow0 + 16 * qb;
+    if (qrow < N) {
+      uint16_t* dqr = dq + hoff + (int64_t)qrow * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int db = 0; db < C::DB; ++db) {
         u32x2 w;
-        w[0] = pack_bf16x2(dqt[cb][4 * r] * scale, dqt[cb][4 * r + 1] * scale);
-        w[1] = pack_bf16x2(dqt[cb][4 * r + 2] * scale, dqt[cb][4 * r + 3] * scale);
-        *reinterpret_cast<u32x2*>(dqr + cb * 32 + 8 * r + 4 * g) = w;
+        w[0] = pack_bf16x2(dqt[qb][db][0] * scale, dqt[qb][db][1] * scale);
+        w[1] = pack_bf16x2(dqt[qb][db][2] * scale, dqt[qb][db][3] * scale);
+        *reinterpret_cast<u32x2*>(dqr + db * 16 + 4 * g) = w;
       }
+    }
   }
 }
 
@@ -608,15 +645,15 @@ int launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const f
   return (int)hipGetLastError();
 }
 
-template <int D>
+template <int D, int RA = kReadAhead, int SA = kStepAhead>
 int launch_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
-              const uint16_t* dO, const float* delta, uint16_t* dq, int64_t BH, int64_t N,
-              float scale, hipStream_t stream) {
+                const uint16_t* dO, const float* delta, uint16_t* dq, int64_t BH, int64_t N,
+                float scale, hipStream_t stream) {
   using C = DqCfg<D>;
-  hipError_t e = allow_lds(bwd_dq_kernel<D>, C::LDS_BYTES);
+  hipError_t e = allow_lds(bwd_dq_kernel<D, RA, SA>, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
   const int nqt = (int)((N + C::BQ - 1) / C::BQ);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * BH)), dim3(C::THREADS),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, RA, SA>), dim3((unsigned)(nqt * BH)), dim3(C::THREADS),
                      C::LDS_BYTES, stream, q, k, v, lse, dO, delta, dq, (int)N, nqt,
                      scale * kLog2e, scale);
   return (int)hipGetLastError();

@@ -25,11 +25,12 @@
 // Transposing read.  ds_read_b64_tr_b16 works on groups of 16 lanes: source
 // lane 4a + b supplies the address of 4 consecutive bf16 values, and result
 // lane i receives element i % 4 of source lanes i/4, i/4 + 4, i/4 + 8 and
-// i/4 + 12.  tr_operand uses it twice to give lane l (column cbase + l % 32,
-// k-group g = l / 32) the values of rows rb + kperm-order keys
-// {4g..4g+3, 8+4g..8+4g+3} of that column: exactly the operand a 32x32x16
-// matrix-core instruction needs when its contraction index runs along the
-// tile's rows and the other operand comes from score accumulators.
+// i/4 + 12.  Two such reads (tr_read_off, tr_read2) give lane l (column
+// cbase + l % 32, k-group g = l / 32) the values of rows
+// {4g..4g+3, 8+4g..8+4g+3} of a 16-row step in that column: exactly the
+// operand a 32x32x16 matrix-core instruction needs when its contraction
+// index runs along the tile's rows and the other operand comes from score
+// accumulators.
 #pragma once
 
 #include "device_common.h"
@@ -88,54 +89,6 @@ __device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t lds,
       : "memory");
 }
 
-// Copies rows [r0, r0 + R) of one head of a [N][D] bf16 matrix into a tile.
-// The R*D/8 chunks go out as 64-chunk wave instructions; wave w of NW issues
-// instructions w, w + NW, ...  Rows at or past the end of `src` read as 0.
-// `wave` must be wave-uniform (an SGPR value).
-template <int D, int R, int NW>
-__device__ __forceinline__ void tile_load(uint16_t* tile, rsrc_t src, int r0, int wave, int lane) {
-  constexpr int NC = D / 8;               // chunks per row
-  constexpr int NI = R * NC / 64;          // wave instructions per tile
-  static_assert((R * NC) % 64 == 0, "whole wave instructions per tile");
-  static_assert(NI % NW == 0, "the same number of instructions for every wave");
-#pragma unroll
-  for (int u = 0; u < NI / NW; ++u) {
-    const int i = wave + u * NW;
-    const int lin = i * 64 + lane;         // physical chunk position in the tile
-    const int row = lin / NC, phys = lin % NC;
-    const int c = phys ^ swz<D>(row);
-    const uint32_t off = (uint32_t)((row * D + c * 8) * 2);
-    lds_dma16(src, off, __builtin_amdgcn_readfirstlane(lds_addr(tile + i * 64 * 8)),
-              __builtin_amdgcn_readfirstlane((uint32_t)(r0 * D * 2)));
-  }
-}
-
-// Row operand: 8 values of logical chunk c of row r.
-template <int D>
-__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r, int c) {
-  return lds_bf16x8(tile + tile_off<D>(r, c));
-}
-
-// Transposed operand: for lane l, column cbase + l % 32 of rows
-// rb + {4g, 4g+1, 4g+2, 4g+3, 8+4g, ..., 8+4g+3} (g = l / 32), in that order.
-// rb must be a multiple of 16 and cbase a multiple of 32.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int rb, int cbase, int lane) {
-  const int i16 = lane & 15, q = lane >> 4;
-  const int a = i16 >> 2, b = i16 & 3, g = q >> 1;
-  const int col = cbase + 16 * (q & 1) + 4 * b;     // 4 consecutive columns
-  const int r1 = rb + 4 * g + a, r2 = r1 + 8;
-  const uint16_t* p1 = tile + tile_off<D>(r1, col >> 3) + (col & 7);
-  const uint16_t* p2 = tile + tile_off<D>(r2, col >> 3) + (col & 7);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p1));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p2));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
-  return as_bf16x8(w);
-}
-
 // ---------------------------------------------------------------------------
 // Swizzled tiles with per-lane offset tables.  When a tile is loaded one
 // instruction at a time (interleaved with other work) and read through
@@ -171,8 +124,10 @@ __device__ __forceinline__ int row_read_off(int lane, int kk) {
   const int r = lane & 31, c = 2 * kk + (lane >> 5);
   return r * D + ((c ^ swz<D>(r)) << 3);
 }
-// Element offset of this lane's half-h transposing read (see tr_operand) of
-// 32-column block cb in rows 0..15.  16-row step t adds t*16*D.
+// Element offset of this lane's half-h transposing read of 32-column block
+// cb in rows 0..15: source rows 4 g + a + 8 h (g = (lane / 16) / 2, a =
+// (lane % 16) / 4), columns 32 cb + 16 ((lane / 16) % 2) + 4 (lane % 4)
+// ..+3.  16-row step t adds t*16*D.
 template <int D>
 __device__ __forceinline__ int tr_read_off(int lane, int cb, int h) {
   const int i16 = lane & 15, q = lane >> 4;
@@ -203,10 +158,16 @@ __device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p
 // operand, runs at a quarter of it; two lanes per row at a half).  Piece p
 // of row rho sits at position p ^ seg_swz<SWZ>(rho): kind 1 keeps the
 // row-operand reads free of bank conflicts, kind 2 the 16 x 16 transposing
-// reads (below), kind 0 is no swizzle.
+// reads (below), kind 3 both, kind 0 is no swizzle.  (A row operand needs
+// the four row quads rho >> 2 of a block on four different positions of one
+// logical piece; a transposing read needs the quads 0, 1 and the quads 2, 3,
+// which one half-wave reads together, on disjoint halves of the row.)
 template <int SWZ>
 __host__ __device__ constexpr int seg_swz(int rho) {
-  return SWZ == 1 ? ((rho >> 2) & 3) : SWZ == 2 ? 2 * ((rho >> 2) & 1) : 0;
+  return SWZ == 1   ? ((rho >> 2) & 3)
+         : SWZ == 2 ? 2 * ((rho >> 2) & 1)
+         : SWZ == 3 ? 2 * ((rho >> 2) & 1) + ((rho >> 3) & 1)
+                    : 0;
 }
 template <int D, int NW, int SWZ>
 __device__ __forceinline__ uint32_t seg_dma_voff(int wave, int lane) {
@@ -227,29 +188,33 @@ __device__ __forceinline__ void seg_dma(uint32_t tile_lds, rsrc_t src, uint32_t 
             row0_bytes + (uint32_t)(u * USTEP));
 }
 // Operands of the 16 x 16 x 32 instruction (device_common.h).
-// Row operand from a kind-1 tile: for 16-row block kb and 32-column k-step
-// kk, lane L takes the 8 values of row 16 kb + L % 16 at columns
-// 32 kk + 8 (L / 16) ..+7.  The 16 lanes of one k-group read 16 rows of one
-// logical piece, which the swizzle spreads over all 64 banks.
+// Row operand from a kind-1 or kind-3 tile: for 16-row block kb and
+// 32-column k-step kk, lane L takes the 8 values of row 16 kb + L % 16 at
+// columns 32 kk + 8 (L / 16) ..+7.  The 16 lanes of one k-group read 16 rows
+// of one logical piece, which the swizzle spreads over all 64 banks.
+template <int SWZ = 1>
 __device__ __forceinline__ uint32_t seg_rowop16_base(int lane) {
+  static_assert(SWZ == 1 || SWZ == 3, "row operands need a kind-1 or kind-3 tile");
   const int rho = lane & 15, g = lane >> 4;
-  return (uint32_t)(64 * rho + 16 * (g ^ seg_swz<1>(rho)));
+  return (uint32_t)(64 * rho + 16 * (g ^ seg_swz<SWZ>(rho)));
 }
 template <int D>
 __host__ __device__ constexpr int seg_rowop16_imm(int kb, int kk) {
   return (kb * (D / 32) + kk) * 1024;
 }
-// Transposed operand from a kind-2 tile: for 32-row step t and 16-column
+// Transposed operand from a kind-2 or kind-3 tile: for 32-row step t and 16-column
 // block cb, lane L (column 16 cb + L % 16, k-group g = L / 16) takes rows
 // 32 t + 4 g + 0..3 (elements 0..3) and 32 t + 16 + 4 g + 0..3 (elements
 // 4..7) of its column: the key order of two 16 x 16 score accumulators of
 // 16 keys each.  Source lane 4 a + b of group g addresses row 4 g + a of the
 // block, columns 16 (cb & 1) + 4 b ..+3; the swizzle puts the rows 4 apart
 // that one half-wave reads on different banks.  Base for blocks of parity e.
+template <int SWZ = 2>
 __device__ __forceinline__ uint32_t seg_trop16_base(int lane, int e) {
+  static_assert(SWZ == 2 || SWZ == 3, "transposing reads need a kind-2 or kind-3 tile");
   const int i16 = lane & 15, g = lane >> 4, a = i16 >> 2, b = i16 & 3;
   const int rho = 4 * g + a;
-  return (uint32_t)(64 * rho + 16 * ((2 * e + (b >> 1)) ^ seg_swz<2>(rho)) + 8 * (b & 1));
+  return (uint32_t)(64 * rho + 16 * ((2 * e + (b >> 1)) ^ seg_swz<SWZ>(rho)) + 8 * (b & 1));
 }
 template <int D>
 __device__ __forceinline__ bf16x8 seg_trop16_read(const uint8_t* lanebase, int t, int cb) {
