@@ -41,7 +41,7 @@ PROTOTYPES = {
 def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m io_aware_softmax_02_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python io_aware_softmax_02_amd/build.py` "
             "(the attention ops have no other implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in PROTOTYPES.items():

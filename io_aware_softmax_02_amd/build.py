@@ -2,7 +2,7 @@
 this file.  Each source compiles to an object under ``_build/`` (in
 parallel), then hipcc links the shared library.  Always recompiles.
 
-    python -m io_aware_softmax_02_amd.build
+    python io_aware_softmax_02_amd/build.py
 """
 
 from __future__ import annotations
