@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps, so that the "
+                         "shader clock has left its idle state (0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle runs (forward+backward)")
@@ -441,6 +444,15 @@ def main():
         fwd()
         bwd()
 
+    # The shader clock ramps up over the first ~30 ms of work after idle
+    # (per-launch trace durations fall by 20% over the first 15 launches);
+    # untimed steps for `settle` seconds bring it to its working level.
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < args.settle:
+        step()
+        torch.cuda.synchronize()
+        settle_steps += 1
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -510,6 +522,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
         "ms_per_step_min": round(per_step[0], 4),

@@ -76,14 +76,18 @@ def trace(db_glob: str, title: str, cmd: str) -> str:
     res = {r[0]: r for r in con.execute(
         "select name, lds_size, vgpr_count, accum_vgpr_count, sgpr_count, grid_x, workgroup_x "
         "from kernels group by name").fetchall()}
+    durs = collections.defaultdict(list)
+    for n, dt in con.execute("select name, duration from kernels"):
+        durs[n].append(dt / 1000.0)
     out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n",
            f"```\n{cmd}\n```\n",
-           "| kernel | calls | total µs | average µs | % | grid (threads) | block | LDS B | arch VGPR | acc VGPR |",
-           "|---|---|---|---|---|---|---|---|---|---|"]
+           "| kernel | calls | total µs | average µs | median µs | % | grid (threads) | block | LDS B | arch VGPR | acc VGPR |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     for n, calls, tot, avg, pct in rows:
         r = res.get(n)
-        out.append(f"| `{short(n)}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.1f} | "
-                   f"{r[5]} | {r[6]} | {r[1]} | {r[2]} | {r[3]} |")
+        d = sorted(durs.get(n, [avg]))
+        out.append(f"| `{short(n)}` | {calls} | {tot:.1f} | {avg:.1f} | {d[len(d) // 2]:.1f} | "
+                   f"{pct:.1f} | {r[5]} | {r[6]} | {r[1]} | {r[2]} | {r[3]} |")
     return "\n".join(out) + "\n"
 
 
@@ -145,7 +149,7 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str) -> dict:
            # the output directories are the ones the two CSVs were read from
            "commands": [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} --kernel-include-regex '{rx}' "
                         f"-f csv -d {os.path.dirname(csv)} -o pmc -- python3 bench.py --steps 2 "
-                        f"--warmup 1 --no-cpu-baseline"
+                        f"--warmup 1 --settle 0 --no-cpu-baseline"
                         for c, csv in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
                        + [f"python -m io_aware_softmax_02_amd.profile_summary traffic "
                           f"{fetch_csv} {write_csv} {out_json}"],
