@@ -137,6 +137,21 @@ def cpu_baseline(w, heads):
                       f"forward+backward, float64 numpy, {dt:.1f} s"}
 
 
+def settle(seconds, dev):
+    """Untimed bf16 products for `seconds`, so that the shader clock has left
+    its idle state before a measurement mode's first timing."""
+    import torch
+    if seconds <= 0:
+        return
+    a = torch.randn(4096, 4096, device=dev).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            torch.matmul(a, a)
+        torch.cuda.synchronize()
+    del a
+
+
 def sweep(args):
     """Forward and fwd+bwd throughput and peak device memory over N at d=128,
     H=16, B=1 (the pages' long-context sizes, 2k .. 128k).  Alongside each
@@ -147,6 +162,7 @@ def sweep(args):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    settle(args.settle, dev)
     stream = torch.cuda.current_stream(dev)
     B, H, d = 1, 16, 128
     for N in (2048, 4096, 8192, 16384, 32768, 65536, 131072):
@@ -194,6 +210,7 @@ def configs(args):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    settle(args.settle, dev)
     stream = torch.cuda.current_stream(dev)
     for name, w in synth.WORKLOADS.items():
         q, k, v, dO = (x.to(dev) for x in synth.make_inputs(w, backward=True))
@@ -236,6 +253,7 @@ def splitkv(args):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    settle(args.settle, dev)
     stream = torch.cuda.current_stream(dev)
     d = 128
     for B, H, N in ((1, 1, 8192), (1, 2, 16384), (1, 1, 65536), (1, 16, 8192)):
@@ -284,6 +302,7 @@ def fp32(args):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    settle(args.settle, dev)
     stream = torch.cuda.current_stream(dev)
     for B, H, N, d in ((1, 1, 64, 64), (1, 16, 2048, 64), (1, 16, 4096, 128), (1, 16, 8192, 128)):
         q, k, v, dO = (x.to(dev) for x in synth.make_qkv(B, H, N, d, torch.float32, seed=9,
@@ -324,6 +343,7 @@ def contrast(args):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    settle(args.settle, dev)
     stream = torch.cuda.current_stream(dev)
     # calibration copy for counter-based traffic (see the headline run)
     cal_src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
