@@ -10,17 +10,19 @@
 // The dQ pass is separate (it recomputes S, P and dP for its own tiles), so
 // every output is written once, in a fixed order, without atomics.
 //
-// Matrix-core layout as in device_common.h.  Each contraction keeps one
-// operand in registers and reads the other from a row-major LDS tile
-// (lds_tile.h): along rows for S, dP and their transposes, and with
-// transposing reads for the operands whose contraction index runs along the
-// tile's rows (Q^T in dK, dO^T in dV, K^T in dQ), in the key/query order of
-// the score accumulators that supply the other operand.
+// Matrix-core layout as in device_common.h (dK/dV on the 32 x 32 x 16 form,
+// dQ on the 16 x 16 x 32 form).  Each contraction keeps one operand in
+// registers and reads the other from an LDS tile (lds_tile.h): along rows
+// for S, dP and their transposes, and with transposing reads for the
+// operands whose contraction index runs along the tile's rows (Q^T in dK,
+// dO^T in dV, K^T in dQ), in the key/query order of the score accumulators
+// that supply the other operand.  dK/dV uses row-major swizzled tiles, dQ
+// row-segment tiles.
 //
-// Streaming: the tiles of the loop are fetched one tile ahead with direct
+// Streaming: the tiles of the loop are fetched ahead with direct
 // buffer->LDS loads (reads past the end of a head return 0, which is what a
-// ragged last tile needs) into the other half of a double-buffered LDS
-// area; one barrier per tile.
+// ragged last tile needs): dQ double-buffers its K/V tiles with one barrier
+// per tile; dK/dV triple-buffers its Q/dO tiles (below).
 #include "lds_tile.h"
 
 namespace fa {

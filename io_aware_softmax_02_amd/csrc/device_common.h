@@ -1,7 +1,7 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, the
 // bf16 matrix-core instruction, and small load/convert utilities.
 //
-// Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, one wave of
+// Matrix-core layout of the dK/dV kernel (v_mfma_f32_32x32x16_bf16, one wave of
 // 64 lanes; l = lane, g = l / 32):
 //   A operand (32 x 16, row r, k):  lane l holds row r = l % 32, the 8 values
 //                                   of its k-group g.
@@ -13,7 +13,8 @@
 // correct whenever both operands enumerate the same k indices in the same
 // (group, element) order; the hardware's internal order of k does not matter.
 //
-// The forward uses the 16 x 16 x 32 form (v_mfma_f32_16x16x32_bf16; g = l / 16):
+// The forward and the dQ pass use the 16 x 16 x 32 form
+// (v_mfma_f32_16x16x32_bf16; g = l / 16):
 //   A operand (16 x 32):  lane l holds row l % 16, the 8 values of k-group g.
 //   B operand (32 x 16):  lane l holds col l % 16, the 8 values of k-group g.
 //   C/D (16 x 16 fp32):   lane l, element i (0..3) holds row 4*g + i, col l % 16.
