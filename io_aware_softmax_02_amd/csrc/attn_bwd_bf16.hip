@@ -437,8 +437,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 //   P^T = 2^(c S^T - LSE log2 e), dS^T = P^T (dP^T - D)   (per-query stats)
 //   dQ^T += K^T dS^T (A = K^T from LDS, B = dS^T from the accumulators)
 // K and V tiles are in row-segment order (lds_tile.h): K is read along rows
-// for S^T and with transposing reads for K^T, so its swizzle (kind 3) serves
-// both; V is read along rows only (kind 1).  Keys past N read as zero rows
+// for S^T and with transposing reads for K^T, V along rows only, and the
+// tiles' swizzle keeps both kinds of read free of bank conflicts.  Keys past
+// N read as zero rows
 // of K and V, so their dS multiplies a zero row of K^T and adds nothing to dQ.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -497,8 +498,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
   const int nkt = (N + C::BK - 1) / C::BK;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-  const uint32_t kvoff = seg_dma_voff<D, C::WAVES, 3>(wave, lane);
-  const uint32_t vvoff = seg_dma_voff<D, C::WAVES, 1>(wave, lane);
+  const uint32_t voff = seg_dma_voff<D, C::WAVES>(wave, lane);
   constexpr int NU = (C::BK / 16) * (D / 32) / C::WAVES;
   static_assert(NU * C::WAVES == (C::BK / 16) * (D / 32), "whole loads per wave");
   auto load_tile = [&](int jt, int b) {
@@ -506,12 +506,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint32_t r0 = (uint32_t)(jt * C::BK * D * 2);
     asm volatile("" : "+s"(kd), "+s"(vd));   // one address per buffer, not one per load
 #pragma unroll
-    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, kvoff, r0, wave, u);
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, voff, r0, wave, u);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, vvoff, r0, wave, u);
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, voff, r0, wave, u);
   };
-  const uint32_t krow = seg_rowop16_base<3>(lane), vrow = seg_rowop16_base<1>(lane);
-  const uint32_t ktr0 = seg_trop16_base<3>(lane, 0), ktr1 = seg_trop16_base<3>(lane, 1);
+  const uint32_t rowop = seg_rowop16_base(lane);
+  const uint32_t ktr0 = seg_trop16_base(lane, 0), ktr1 = seg_trop16_base(lane, 1);
   load_tile(0, 0);
   wait_vmem();
   __syncthreads();
@@ -547,15 +547,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         bf16x8 ka[RA + 1], va[RA + 1];
 #pragma unroll
         for (int n = 0; n < RA; ++n) {
-          ka[n] = rd(kt8 + krow, n);
-          va[n] = rd(vt8 + vrow, n);
+          ka[n] = rd(kt8 + rowop, n);
+          va[n] = rd(vt8 + rowop, n);
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           if (n + RA < NS) {
-            ka[(n + RA) % (RA + 1)] = rd(kt8 + krow, n + RA);
-            va[(n + RA) % (RA + 1)] = rd(vt8 + vrow, n + RA);
+            ka[(n + RA) % (RA + 1)] = rd(kt8 + rowop, n + RA);
+            va[(n + RA) % (RA + 1)] = rd(vt8 + rowop, n + RA);
           }
           __builtin_amdgcn_sched_barrier(0);
           const int kk = n / 2, h = n % 2;

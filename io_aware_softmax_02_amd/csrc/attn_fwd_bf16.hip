@@ -128,12 +128,11 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
   const int nkt = (N + BC - 1) / BC;
   const int j0 = SPLIT ? (int)((int64_t)part * nkt / nsplit) : 0;
   const int j1 = SPLIT ? (int)((int64_t)(part + 1) * nkt / nsplit) : nkt;
-  // K and V tiles in row-segment order (lds_tile.h), K swizzled for its
-  // row-operand reads and V for its transposing reads; buffer b at byte
-  // b * BUF_ELEMS * 2, K then V.
+  // K and V tiles in row-segment order (lds_tile.h), whose swizzle keeps
+  // both K's row-operand reads and V's transposing reads free of bank
+  // conflicts; buffer b at byte b * BUF_ELEMS * 2, K then V.
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-  const uint32_t kvoff = seg_dma_voff<D, C::WAVES, 1>(wave, lane);
-  const uint32_t vvoff = seg_dma_voff<D, C::WAVES, 2>(wave, lane);
+  const uint32_t voff = seg_dma_voff<D, C::WAVES>(wave, lane);
   constexpr int NU = (BC / 16) * (D / 32) / C::WAVES;
   static_assert(NU * C::WAVES == (BC / 16) * (D / 32), "whole loads per wave");
   auto load_tile = [&](int jt, int b) {
@@ -141,9 +140,9 @@ __global__ __launch_bounds__(64 * NWAVES, MINW) void fwd_bf16_kernel(
     const uint32_t r0 = (uint32_t)(jt * BC * D * 2);
     asm volatile("" : "+s"(kd), "+s"(vd));   // one address per buffer, not one per load
 #pragma unroll
-    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, kvoff, r0, wave, u);
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(kd, rk, voff, r0, wave, u);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, vvoff, r0, wave, u);
+    for (int u = 0; u < NU; ++u) seg_dma<D, C::WAVES>(vd, rv, voff, r0, wave, u);
   };
   const uint32_t kbase = seg_rowop16_base(lane);
   const uint32_t vbase0 = seg_trop16_base(lane, 0), vbase1 = seg_trop16_base(lane, 1);

@@ -3,9 +3,12 @@
 //
 // Layout.  A tile holds rows of D bf16 values (2*D bytes, no padding).  Each
 // row is a sequence of 16-byte chunks; logical chunk c of row r is stored at
-// physical chunk c ^ swz<D>(r).  LDS has 64 banks of 4 bytes; a 16-byte
-// read is served 16 lanes at a time and an 8-byte read 32 lanes at a time,
-// so the swizzle is chosen to make both read patterns conflict-free:
+// physical chunk c ^ swz<D>(r).  LDS has 64 banks of 4 bytes; the swizzle
+// keeps both read patterns below conflict-free (SQ_LDS_BANK_CONFLICT is 0
+// for the kernel that uses these tiles).  It was chosen for groups of 16
+// consecutive lanes, which 16-byte reads are not served in (row-segment
+// tiles below), but on these patterns the measured groups see distinct
+// banks as well:
 //   - row operands: 16 consecutive rows, one logical chunk each.  With
 //     D = 128 a row spans all 64 banks and the bank group is the physical
 //     chunk, so swz must take 16 distinct values on 16 consecutive rows;
@@ -156,25 +159,23 @@ __device__ __forceinline__ bf16x8 tr_read2(const uint16_t* p1, const uint16_t* p
 // when every four consecutive lanes read one contiguous 64-byte segment
 // (a load whose lanes cover 32 rows x 32 bytes, the order of a matrix-core
 // operand, runs at a quarter of it; two lanes per row at a half).  Piece p
-// of row rho sits at position p ^ seg_swz<SWZ>(rho): kind 1 keeps the
-// row-operand reads free of bank conflicts, kind 2 the 16 x 16 transposing
-// reads (below), kind 3 both, kind 0 is no swizzle.  (A row operand needs
-// the four row quads rho >> 2 of a block on four different positions of one
-// logical piece; a transposing read needs the quads 0, 1 and the quads 2, 3,
-// which one half-wave reads together, on disjoint halves of the row.)
-template <int SWZ>
-__host__ __device__ constexpr int seg_swz(int rho) {
-  return SWZ == 1   ? ((rho >> 2) & 3)
-         : SWZ == 2 ? 2 * ((rho >> 2) & 1)
-         : SWZ == 3 ? 2 * ((rho >> 2) & 1) + ((rho >> 3) & 1)
-                    : 0;
-}
-template <int D, int NW, int SWZ>
+// of row rho sits at position p ^ seg_swz(rho).
+// LDS service order (measured with SQ_LDS_BANK_CONFLICT on synthetic lane
+// patterns): a 16-byte read (ds_read_b128) is served in four groups of 16
+// lanes, each group the lanes of one half-wave whose lane bits 2, 3 and 4
+// have the same parity, and a group is conflict-free when its 16 reads fall
+// on 16 different 4-bank groups; 8-byte transposing reads showed no
+// conflicts on these tiles.  Flipping bit 1 of the piece by bit 2 of the row
+// makes both the row-operand reads and the transposing reads below
+// conflict-free (without a swizzle, or with one chosen for 16 consecutive
+// lanes, every row-operand read costs a second pass).
+__host__ __device__ constexpr int seg_swz(int rho) { return 2 * ((rho >> 2) & 1); }
+template <int D, int NW>
 __device__ __forceinline__ uint32_t seg_dma_voff(int wave, int lane) {
   constexpr int C32 = D / 32;
   static_assert(NW % C32 == 0, "whole 16-row steps between a wave's instructions");
   const int rho = lane >> 2, pos = lane & 3;
-  const int p = pos ^ seg_swz<SWZ>(rho);
+  const int p = pos ^ seg_swz(rho);
   const int row = (wave / C32) * 16 + rho, col = (wave % C32) * 32 + p * 8;
   return (uint32_t)((row * D + col) * 2);
 }
@@ -188,33 +189,26 @@ __device__ __forceinline__ void seg_dma(uint32_t tile_lds, rsrc_t src, uint32_t 
             row0_bytes + (uint32_t)(u * USTEP));
 }
 // Operands of the 16 x 16 x 32 instruction (device_common.h).
-// Row operand from a kind-1 or kind-3 tile: for 16-row block kb and
-// 32-column k-step kk, lane L takes the 8 values of row 16 kb + L % 16 at
-// columns 32 kk + 8 (L / 16) ..+7.  The 16 lanes of one k-group read 16 rows
-// of one logical piece, which the swizzle spreads over all 64 banks.
-template <int SWZ = 1>
+// Row operand: for 16-row block kb and 32-column k-step kk, lane L takes
+// the 8 values of row 16 kb + L % 16 at columns 32 kk + 8 (L / 16) ..+7.
 __device__ __forceinline__ uint32_t seg_rowop16_base(int lane) {
-  static_assert(SWZ == 1 || SWZ == 3, "row operands need a kind-1 or kind-3 tile");
   const int rho = lane & 15, g = lane >> 4;
-  return (uint32_t)(64 * rho + 16 * (g ^ seg_swz<SWZ>(rho)));
+  return (uint32_t)(64 * rho + 16 * (g ^ seg_swz(rho)));
 }
 template <int D>
 __host__ __device__ constexpr int seg_rowop16_imm(int kb, int kk) {
   return (kb * (D / 32) + kk) * 1024;
 }
-// Transposed operand from a kind-2 or kind-3 tile: for 32-row step t and 16-column
-// block cb, lane L (column 16 cb + L % 16, k-group g = L / 16) takes rows
-// 32 t + 4 g + 0..3 (elements 0..3) and 32 t + 16 + 4 g + 0..3 (elements
-// 4..7) of its column: the key order of two 16 x 16 score accumulators of
-// 16 keys each.  Source lane 4 a + b of group g addresses row 4 g + a of the
-// block, columns 16 (cb & 1) + 4 b ..+3; the swizzle puts the rows 4 apart
-// that one half-wave reads on different banks.  Base for blocks of parity e.
-template <int SWZ = 2>
+// Transposed operand: for 32-row step t and 16-column block cb, lane L
+// (column 16 cb + L % 16, k-group g = L / 16) takes rows 32 t + 4 g + 0..3
+// (elements 0..3) and 32 t + 16 + 4 g + 0..3 (elements 4..7) of its column:
+// the key order of two 16 x 16 score accumulators of 16 keys each.  Source
+// lane 4 a + b of group g addresses row 4 g + a of the block, columns
+// 16 (cb & 1) + 4 b ..+3.  Base for blocks of parity e.
 __device__ __forceinline__ uint32_t seg_trop16_base(int lane, int e) {
-  static_assert(SWZ == 2 || SWZ == 3, "transposing reads need a kind-2 or kind-3 tile");
   const int i16 = lane & 15, g = lane >> 4, a = i16 >> 2, b = i16 & 3;
   const int rho = 4 * g + a;
-  return (uint32_t)(64 * rho + 16 * ((2 * e + (b >> 1)) ^ seg_swz<SWZ>(rho)) + 8 * (b & 1));
+  return (uint32_t)(64 * rho + 16 * ((2 * e + (b >> 1)) ^ seg_swz(rho)) + 8 * (b & 1));
 }
 template <int D>
 __device__ __forceinline__ bf16x8 seg_trop16_read(const uint8_t* lanebase, int t, int cb) {
