@@ -42,3 +42,28 @@ def test_configs_markdown(tmp_path):
     md = configs_md(str(log))
     row = [r for r in md.splitlines() if r.startswith("| `w`")]
     assert row == ["| `w` | 1, 2, 3, 64 | bf16 | 500.0 | 100.0 | 1500.0 | 250.0 | 10.0 |"]
+
+
+def test_trace_markdown_average_and_median(tmp_path):
+    # A kernel-trace database with the two tables the summary reads: the
+    # median column is the middle per-launch duration, which stays at the
+    # working-clock value when the first launches run slow after idle.
+    import sqlite3
+    from io_aware_softmax_02_amd.profile_summary import trace
+    db = tmp_path / "t_results.db"
+    con = sqlite3.connect(str(db))
+    con.execute("create table kernels (name text, duration integer, lds_size integer, "
+                "vgpr_count integer, accum_vgpr_count integer, sgpr_count integer, "
+                "grid_x integer, workgroup_x integer)")
+    durs_ns = [1500000, 1200000, 1000000, 1000000, 1000000]
+    for d in durs_ns:
+        con.execute("insert into kernels values ('void fa::k<128>(int)', ?, 1024, 128, 0, 32, "
+                    "262144, 256)", (d,))
+    con.execute("create table top_kernels (name text, total_calls integer, "
+                "total_duration real, average real, percentage real)")
+    con.execute("insert into top_kernels values ('void fa::k<128>(int)', 5, 5700.0, 1140.0, 100.0)")
+    con.commit()
+    con.close()
+    md = trace(str(tmp_path / "*_results.db"), "T", "C")
+    row = [r for r in md.splitlines() if r.startswith("| `k<128>`")]
+    assert row == ["| `k<128>` | 5 | 5700.0 | 1140.0 | 1000.0 | 100.0 | 262144 | 256 | 1024 | 128 | 0 |"]
