@@ -48,12 +48,6 @@ __device__ __forceinline__ int swz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// Offset (bf16 elements) of logical chunk c of row r in a tile with D columns.
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) {
-  return r * D + ((c ^ swz<D>(r)) << 3);
-}
-
 // LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
