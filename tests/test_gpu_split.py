@@ -110,3 +110,54 @@ def test_split_count_errors():
         with pytest.raises(fa.FAError) as e:
             fa.fa_fwd_split(qd, kd, vd, bad)
         assert "FA_ERR_SHAPE" in str(e.value)
+
+
+def test_split_and_merge_at_n131072_sampled_rows():
+    """Split-KV forward and merge at the very long sequence length (N =
+    131072, d = 128, two heads, four key ranges), checked on sampled rows:
+    the first and last row, the first row of every range and 48 seeded rows.
+    Each part against the oracle on its key range, the merge against the
+    oracle on all keys, and the merge against fa_fwd."""
+    B, H, N, d, P = 1, 2, 131072, 128, 4
+    say(f"case split B={B} H={H} N={N} d={d} n_split={P}")
+    q, k, v, _ = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=13)
+    scale = synth.default_scale(d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    op, lp = fa.fa_fwd_split(qd, kd, vd, P, scale)
+    o, l = fa.fa_merge(op, lp)
+    O, L = fa.fa_fwd(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    bounds = oracle.split_bounds(N, P, tile_of(d))
+    rng = np.random.default_rng(13)
+    worst = [0.0, 0.0, 0.0, 0.0, 0.0]
+    num = den = 0.0    # relative Frobenius error of the merged O on the rows
+    for h in range(H):
+        rows = np.unique(np.concatenate([[0, N - 1], [a for a, _ in bounds],
+                                         rng.choice(N, size=48, replace=False)]))
+        ri = torch.from_numpy(rows).to(DEV)
+        qn, kn, vn = f64(q[0, h])[rows], f64(k[0, h]), f64(v[0, h])
+        Oref, Lref = oracle.sdpa_rows(qn, kn, vn, scale)
+        Op, Lp = oracle.sdpa_split_head(qn, kn, vn, scale, bounds)
+        og, lg = f64(o[0, h].index_select(0, ri)), f64(l[0, h].index_select(0, ri))
+        opg = f64(op[:, 0, h].index_select(1, ri))
+        lpg = f64(lp[:, 0, h].index_select(1, ri))
+        worst[0] = max(worst[0], max_abs(og, Oref))
+        worst[1] = max(worst[1], mean_abs(og, Oref))
+        worst[2] = max(worst[2], max_abs(lg, Lref))
+        worst[3] = max(worst[3], max_abs(opg, Op))
+        worst[4] = max(worst[4], max_abs(lpg, Lp))
+        num += float(((og - Oref) ** 2).sum())
+        den += float((Oref ** 2).sum())
+    say(f"  merged: O max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} LSE max-abs {worst[2]:.3e}; "
+        f"parts: O max-abs {worst[3]:.3e} LSE max-abs {worst[4]:.3e}")
+    assert worst[0] <= TOL_BF16_O_MAX and worst[1] <= TOL_BF16_O_MEAN
+    assert worst[2] <= TOL_BF16_LSE_MAX
+    assert worst[3] <= TOL_BF16_O_MAX and worst[4] <= TOL_BF16_LSE_MAX
+    # At this N, O rows average very many keys and are small, so the absolute
+    # bounds are loose; relative to its size, O is within a few bf16 roundings.
+    rel = math.sqrt(num / den)
+    say(f"  merged O relative Frobenius {rel:.3e}")
+    assert rel <= 2e-2
+    # the merged result and the plain forward agree to bf16 output rounding
+    assert float((o.float() - O.float()).abs().max()) <= TOL_BF16_O_MAX
+    assert float((l - L).abs().max()) <= TOL_BF16_LSE_MAX
