@@ -180,16 +180,23 @@ def test_vlong_forward_sampled_rows_and_memory():
     Oh, Lh = f64(o).reshape(w.B * w.H, w.N, w.d), f64(lse).reshape(w.B * w.H, w.N)
     qf, kf, vf = (f64(x).reshape(w.B * w.H, w.N, w.d) for x in (q, k, v))
     worst = [0.0, 0.0, 0.0]
+    num = den = 0.0
     for bh in range(w.B * w.H):
         r = rows[bh]
         Oref, Lref = oracle.sdpa_rows(qf[bh][r], kf[bh], vf[bh], w.scale)
         worst[0] = max(worst[0], max_abs(Oh[bh][r], Oref))
         worst[1] = max(worst[1], mean_abs(Oh[bh][r], Oref))
         worst[2] = max(worst[2], max_abs(Lh[bh][r], Lref))
+        num += float(((Oh[bh][r] - Oref) ** 2).sum())
+        den += float((Oref ** 2).sum())
+    rel = math.sqrt(num / den)
     say(f"  sampled rows: O max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} "
-        f"LSE max-abs {worst[2]:.3e}")
+        f"LSE max-abs {worst[2]:.3e}; O relative Frobenius {rel:.3e}")
     assert worst[0] <= TOL_BF16_O_MAX and worst[1] <= TOL_BF16_O_MEAN
     assert worst[2] <= TOL_BF16_LSE_MAX
+    # O rows average very many keys here and are small, so the absolute
+    # bounds are loose; relative to its size, O is within a few bf16 roundings.
+    assert rel <= 2e-2
 
 
 def run_bf16_fwd_bwd(q, k, v, dO, scale):
