@@ -47,10 +47,16 @@ def oracle_fwd(name, q, k, v, scale, heads=None):
 
 
 def check_fwd_bf16(O, L, Oref, Lref, label):
+    """The stated bf16 bounds, plus O within 2e-2 relative Frobenius of the
+    reference: the absolute bounds alone are loose where O rows average many
+    keys and are small (bf16 output rounding alone is ~2e-3 relative)."""
     o, l = f64(O), f64(L)
     ma, mn, ml = max_abs(o, Oref), mean_abs(o, Oref), max_abs(l, Lref)
-    say(f"{label}: O max-abs {ma:.3e} mean-abs {mn:.3e}  LSE max-abs {ml:.3e}")
+    rel = grad_err(o, Oref)
+    say(f"{label}: O max-abs {ma:.3e} mean-abs {mn:.3e} rel-Frobenius {rel:.3e}  "
+        f"LSE max-abs {ml:.3e}")
     assert ma <= TOL_BF16_O_MAX and mn <= TOL_BF16_O_MEAN and ml <= TOL_BF16_LSE_MAX
+    assert rel <= 2e-2
 
 
 def grad_err(x, ref):
