@@ -67,6 +67,9 @@ def parse():
                     help="fp32 path measurement instead of the headline one")
     ap.add_argument("--contrast", action="store_true",
                     help="materialised standard attention beside fa_fwd instead of the headline")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="the fp64 oracle timed on a bounded sample of every named workload "
+                         "(host cores only) instead of the headline")
     ap.add_argument("--configs", action="store_true",
                     help="forward and fwd+bwd throughput on every named workload instead of "
                          "the headline")
@@ -110,17 +113,76 @@ def measured_traffic(kernel):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+CPU_SAMPLE_HEADS = 4   # heads per workload the oracle runs in full for --cpu-configs
+
+
+def cpu_configs(args):
+    """The fp64 oracle (the CPU baseline, not tuned) timed on a bounded
+    sample of each named workload: up to CPU_SAMPLE_HEADS heads in full (forward, and
+    backward where the workload has one), and for the very long workload its
+    sampled query rows against all keys.  Each line states the sample; the
+    per-row time scaled to all rows and heads is labelled as an
+    extrapolation."""
+    import numpy as np
+    import oracle
+    import synth
+    f64 = synth.to_f64
+    threads = blas_threads()
+    for name, w in synth.WORKLOADS.items():
+        q, k, v, dO = synth.make_inputs(w)
+        BH = w.B * w.H
+        qf, kf, vf = (f64(x).reshape(BH, w.N, w.d) for x in (q, k, v))
+        line = {"cpu_oracle": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "cores": threads}
+        if w.sample_rows is not None:
+            rows = synth.sampled_rows(w)
+            t0 = time.perf_counter()
+            for bh in range(BH):
+                oracle.sdpa_rows(qf[bh][rows[bh]], kf[bh], vf[bh], w.scale)
+            dt = time.perf_counter() - t0
+            nrows = BH * w.sample_rows
+            flops = 4.0 * nrows * w.N * w.d
+            line.update({"sample": f"{w.sample_rows} sampled query rows x {BH} heads against all "
+                                   f"{w.N} keys, forward",
+                         "seconds": round(dt, 2), "tflops": flops / dt / 1e12,
+                         "extrapolated_full_forward_seconds": round(dt * (BH * w.N) / nrows, 1)})
+        else:
+            nh = min(BH, CPU_SAMPLE_HEADS)
+            t0 = time.perf_counter()
+            oracle.sdpa_forward(qf[:nh], kf[:nh], vf[:nh], w.scale)
+            dtf = time.perf_counter() - t0
+            flops = w.fwd_flops() * nh / BH
+            dt = dtf
+            what = "forward"
+            if w.backward:
+                gf = f64(dO).reshape(BH, w.N, w.d)
+                t0 = time.perf_counter()
+                oracle.sdpa_backward(qf[:nh], kf[:nh], vf[:nh], gf[:nh], w.scale)
+                dt += time.perf_counter() - t0
+                flops += w.bwd_flops() * nh / BH
+                what = "forward + backward"
+            line.update({"sample": f"{nh} of {BH} heads, {what}", "seconds": round(dt, 2),
+                         "tflops": flops / dt / 1e12,
+                         "extrapolated_all_heads_seconds": round(dt * BH / nh, 1)})
+        print(json.dumps(line), flush=True)
+        del q, k, v, dO, qf, kf, vf
+    del np
+
+
 def cpu_baseline(w, heads):
     """The fp64 oracle (forward + backward, materialising S and P) on `heads`
     of the workload's heads; returns a dict in the metric's unit."""
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     q, k, v, dO = synth.make_inputs(w)
     sel = list(range(heads))
     f64 = synth.to_f64
@@ -422,6 +484,8 @@ def main():
         return contrast(args)
     if args.configs:
         return configs(args)
+    if args.cpu_configs:
+        return cpu_configs(args)
     if args.fp32:
         return fp32(args)
 

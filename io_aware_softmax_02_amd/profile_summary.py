@@ -19,6 +19,8 @@ leaves in its output directory into the short text summaries that are kept:
       the JSON lines of `bench.py --contrast` as markdown
   python -m io_aware_softmax_02_amd.profile_summary configs LOG
       the JSON lines of `bench.py --configs` as markdown
+  python -m io_aware_softmax_02_amd.profile_summary cpu LOG
+      the JSON lines of `bench.py --cpu-configs` as markdown
   python -m io_aware_softmax_02_amd.profile_summary sweep LOG
   python -m io_aware_softmax_02_amd.profile_summary splitkv LOG
       the JSON lines of `bench.py --sweep` / `bench.py --splitkv` as markdown
@@ -251,6 +253,28 @@ def configs_md(path: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def cpu_md(path: str) -> str:
+    rows = list(_json_lines(path))
+    cores = sorted({r["cores"] for r in rows})
+    out = ["# The fp64 oracle on the host cores, every named workload\n",
+           "Command (repository root, on the GPU box's host; no GPU work): "
+           "`python bench.py --cpu-configs > LOG; "
+           "python -m io_aware_softmax_02_amd.profile_summary cpu LOG`\n",
+           "The oracle as it stands (numpy float64, materialising S and P), timed on a bounded "
+           "sample of each workload with "
+           f"{', '.join(str(c) for c in cores)} BLAS threads. TF/s counts the same work as the "
+           "GPU figures (forward 4·B·H·N²·d per head or per row share, backward 2.5× the "
+           "forward). The last column scales the sample's time to the whole workload and is an "
+           "**extrapolation**, not a measurement.\n",
+           "| workload | B, H, N, d | sample | seconds | TF/s | whole workload, extrapolated s |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        ext = r.get("extrapolated_all_heads_seconds", r.get("extrapolated_full_forward_seconds"))
+        out.append(f"| `{r['cpu_oracle']}` | {r['B']}, {r['H']}, {r['N']}, {r['d']} | "
+                   f"{r['sample']} | {r['seconds']} | {r['tflops']:.4f} | {ext} |")
+    return "\n".join(out) + "\n"
+
+
 def splitkv_md(path: str) -> str:
     out = ["# Split-KV forward + merge against the plain forward (bf16, d = 128)\n",
            "Command (repository root, one MI355X): `python bench.py --splitkv > LOG; "
@@ -288,6 +312,8 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(contrast_md(argv[2]))
     elif cmd == "configs":
         sys.stdout.write(configs_md(argv[2]))
+    elif cmd == "cpu":
+        sys.stdout.write(cpu_md(argv[2]))
     elif cmd == "sweep":
         sys.stdout.write(sweep_md(argv[2]))
     elif cmd == "splitkv":

@@ -67,3 +67,20 @@ def test_trace_markdown_average_and_median(tmp_path):
     md = trace(str(tmp_path / "*_results.db"), "T", "C")
     row = [r for r in md.splitlines() if r.startswith("| `k<128>`")]
     assert row == ["| `k<128>` | 5 | 5700.0 | 1140.0 | 1000.0 | 100.0 | 262144 | 256 | 1024 | 128 | 0 |"]
+
+
+def test_cpu_markdown_labels_extrapolation(tmp_path):
+    from io_aware_softmax_02_amd.profile_summary import cpu_md
+    lines = [{"cpu_oracle": "a", "B": 1, "H": 2, "N": 8, "d": 4, "cores": 16,
+              "sample": "1 of 2 heads, forward", "seconds": 1.5, "tflops": 0.25,
+              "extrapolated_all_heads_seconds": 3.0},
+             {"cpu_oracle": "b", "B": 1, "H": 1, "N": 9, "d": 4, "cores": 16,
+              "sample": "2 sampled query rows", "seconds": 0.5, "tflops": 0.125,
+              "extrapolated_full_forward_seconds": 2.25}]
+    log = tmp_path / "log"
+    log.write_text("\n".join(json.dumps(x) for x in lines) + "\n")
+    md = cpu_md(str(log))
+    assert "**extrapolation**" in md and "16 BLAS threads" in md
+    rows = [r for r in md.splitlines() if r.startswith("| `")]
+    assert rows == ["| `a` | 1, 2, 8, 4 | 1 of 2 heads, forward | 1.5 | 0.2500 | 3.0 |",
+                    "| `b` | 1, 1, 9, 4 | 2 sampled query rows | 0.5 | 0.1250 | 2.25 |"]
