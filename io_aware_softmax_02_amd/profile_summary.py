@@ -19,9 +19,6 @@ leaves in its output directory into the short text summaries that are kept:
       the JSON lines of `bench.py --contrast` as markdown
   python -m io_aware_softmax_02_amd.profile_summary configs LOG
       the JSON lines of `bench.py --configs` as markdown
-  python -m io_aware_softmax_02_amd.profile_summary probe CSV LOG TITLE COMMAND
-      per-pattern LDS counters of the lds_service_order probe (its --pmc CSV
-      and the pattern table it printed) as markdown
   python -m io_aware_softmax_02_amd.profile_summary cpu LOG
       the JSON lines of `bench.py --cpu-configs` as markdown
   python -m io_aware_softmax_02_amd.profile_summary sweep LOG
@@ -278,38 +275,6 @@ def cpu_md(path: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def probe_md(csv_path: str, log_path: str, title: str, cmd: str) -> str:
-    names = {}
-    for line in open(log_path):
-        m = re.match(r"pattern\s+(\d+): (.*)$", line.strip())
-        if m:
-            names[int(m.group(1))] = m.group(2)
-    agg = collections.defaultdict(lambda: collections.defaultdict(float))
-    disp = collections.defaultdict(set)
-    for r in csv.DictReader(open(csv_path)):
-        m = re.search(r"probe<(\d+), (\d+)>", r["Kernel_Name"])
-        if not m:
-            continue
-        key = (int(m.group(1)), int(m.group(2)))
-        agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
-        disp[key].add(r["Dispatch_Id"])
-    out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n",
-           f"```\n{cmd}\n```\n",
-           "Per pattern: LDS instructions, bank-conflict cycles and LDS-busy cycles per "
-           "instruction (counters summed over the chip, one dispatch of 1024 one-wave "
-           "workgroups, 4096 reads each). A conflict-free 16-byte read keeps the LDS busy "
-           "≈ 4 cycles, an 8-byte one ≈ 2.\n",
-           "| # | pattern | read | instructions | conflict cycles / instr. | LDS-busy cycles / instr. |",
-           "|---|---|---|---|---|---|"]
-    for (kind, i) in sorted(agg, key=lambda x: x[1]):
-        c = {k: v / len(disp[(kind, i)]) for k, v in agg[(kind, i)].items()}
-        n = c.get("SQ_INSTS_LDS", 0.0)
-        out.append(f"| {i} | {names.get(i, '?')} | {'ds_read_b128' if kind == 0 else 'ds_read_b64_tr_b16'} | "
-                   f"{n:,.0f} | {c.get('SQ_LDS_BANK_CONFLICT', 0.0) / n:.2f} | "
-                   f"{c.get('SQ_LDS_IDX_ACTIVE', 0.0) / n:.2f} |")
-    return "\n".join(out) + "\n"
-
-
 def splitkv_md(path: str) -> str:
     out = ["# Split-KV forward + merge against the plain forward (bf16, d = 128)\n",
            "Command (repository root, one MI355X): `python bench.py --splitkv > LOG; "
@@ -347,8 +312,6 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(contrast_md(argv[2]))
     elif cmd == "configs":
         sys.stdout.write(configs_md(argv[2]))
-    elif cmd == "probe":
-        sys.stdout.write(probe_md(argv[2], argv[3], argv[4], argv[5]))
     elif cmd == "cpu":
         sys.stdout.write(cpu_md(argv[2]))
     elif cmd == "sweep":

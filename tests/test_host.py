@@ -84,20 +84,3 @@ def test_cpu_markdown_labels_extrapolation(tmp_path):
     rows = [r for r in md.splitlines() if r.startswith("| `")]
     assert rows == ["| `a` | 1, 2, 8, 4 | 1 of 2 heads, forward | 1.5 | 0.2500 | 3.0 |",
                     "| `b` | 1, 1, 9, 4 | 2 sampled query rows | 0.5 | 0.1250 | 2.25 |"]
-
-
-def test_probe_markdown_joins_pattern_names_and_counters(tmp_path):
-    from io_aware_softmax_02_amd.profile_summary import probe_md
-    log = tmp_path / "log"
-    log.write_text("pattern  0: linear\npattern  1: rotated\nstatus no error\n")
-    csvp = tmp_path / "c.csv"
-    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
-    for d, k, inst, conf, act in ((1, "void probe<0, 0>(unsigned int const*, unsigned int*)", 100, 0, 400),
-                                  (2, "void probe<0, 1>(unsigned int const*, unsigned int*)", 100, 400, 800)):
-        rows += [f'{d},"{k}",SQ_INSTS_LDS,{inst}', f'{d},"{k}",SQ_LDS_BANK_CONFLICT,{conf}',
-                 f'{d},"{k}",SQ_LDS_IDX_ACTIVE,{act}']
-    csvp.write_text("\n".join(rows) + "\n")
-    md = probe_md(str(csvp), str(log), "T", "C")
-    body = [r for r in md.splitlines() if r.startswith("| 0 ") or r.startswith("| 1 ")]
-    assert body == ["| 0 | linear | ds_read_b128 | 100 | 0.00 | 4.00 |",
-                    "| 1 | rotated | ds_read_b128 | 100 | 4.00 | 8.00 |"]
