@@ -24,6 +24,7 @@ from .attention import (  # noqa: F401
     sdpa_forward_head,
     sdpa_backward,
     sdpa_backward_head,
+    sdpa_backward_rows,
     sdpa_rows,
     online_forward_head,
     online_forward_normalised_head,

@@ -39,6 +39,7 @@ __all__ = [
     "sdpa_forward",
     "sdpa_rows",
     "sdpa_backward_head",
+    "sdpa_backward_rows",
     "sdpa_backward",
     "online_forward_head",
     "online_forward_normalised_head",
@@ -130,6 +131,23 @@ def sdpa_backward_head(q, k, v, dO, scale: float):
     return dict(dQ=dQ, dK=dK, dV=dV, O=O, LSE=lse, D=D, P=P, dP=dP, dS=dS)
 
 
+def sdpa_backward_rows(q_rows, k, v, dO_rows, scale: float):
+    """dQ and D for selected query rows of one head against the full K and V.
+
+    Row i of dQ needs only q_i, dO_i and all keys: P_i = softmax(s q_i K^T),
+    O_i = P_i V, D_i = dO_i . O_i, dP_i = dO_i V^T, dS_i = P_i * (dP_i - D_i),
+    dQ_i = s dS_i K.  So a row subset is the plain backward restricted to those
+    rows (dK and dV, which sum over every query, are not formed).
+    Returns (dQ_rows [R, d], D_rows [R])."""
+    q, k, v, dO = _f64(q_rows), _f64(k), _f64(v), _f64(dO_rows)
+    s = float(scale)
+    P, _, _ = softmax_rows(s * (q @ k.T))
+    O = P @ v
+    D = (dO * O).sum(axis=-1)
+    dS = P * ((dO @ v.T) - D[:, None])
+    return s * (dS @ k), D
+
+
 def sdpa_backward(q, k, v, dO, scale: float, heads: Optional[Iterable[int]] = None):
     """Analytic backward over [..., N, d] arrays.  Returns (dQ, dK, dV, D).
 
@@ -195,12 +213,19 @@ def online_forward_head(q, k, v, scale: float, block: int = 8,
 
 def online_forward_normalised_head(q, k, v, scale: float, block: int = 8,
                                    order: Optional[Sequence[int]] = None):
-    """One pass keeping O normalised after every block ([P2] section 六,
-    the O_new formula): O_new = diag(alpha) O_old * (l_old / l_new)
-    + P~ V_b / l_new, with l_new = alpha l_old + rowsum P~.  The page writes
-    the first term as O_old / (l_new / l_old); it is evaluated here as
-    O_old * (l_old / l_new), which is the same number and avoids 0/0 on the
-    first block where l_old = 0."""
+    """One pass in which the output is, after every block, the attention
+    output over the keys seen so far ([P2] section 六 keeps O normalised this
+    way).
+
+    Derivation used here: the keys seen so far carry total weight
+    w_old = alpha * l_old against the new reference m' (alpha = exp(m - m')),
+    and the new block carries w_b = rowsum P~ with P~ = exp(S_b - m').  The
+    output over all of them is the weighted mean of the two partial outputs,
+        O = (w_old O_old + w_b A_b) / (w_old + w_b),   A_b = P~ V_b / w_b,
+    i.e. the merge of two partial results by their weights (the same rescale
+    identity, [P3] "兩大核心魔法").  Written as theta O_old + (1 - theta) A_b
+    with theta = w_old / (w_old + w_b), it needs no division by l_old, so the
+    first block (l_old = 0, theta = 0) is not a special case."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     nq = q.shape[0]
     m = np.full(nq, -np.inf)
@@ -209,11 +234,13 @@ def online_forward_normalised_head(q, k, v, scale: float, block: int = 8,
     for a, b in _blocks(k.shape[0], block, order):
         Sb = float(scale) * (q @ k[a:b].T)
         m_new = np.maximum(m, Sb.max(axis=1))
-        alpha = np.exp(m - m_new)
+        w_old = np.exp(m - m_new) * l
         Pt = np.exp(Sb - m_new[:, None])
-        l_new = alpha * l + Pt.sum(axis=1)
-        O = (alpha * l / l_new)[:, None] * O + (Pt @ v[a:b]) / l_new[:, None]
-        l, m = l_new, m_new
+        w_b = Pt.sum(axis=1)
+        A_b = (Pt @ v[a:b]) / w_b[:, None]
+        theta = w_old / (w_old + w_b)
+        O = theta[:, None] * O + (1.0 - theta)[:, None] * A_b
+        l, m = w_old + w_b, m_new
     return O, m + np.log(l)
 
 

@@ -476,3 +476,98 @@ def _mut_merge_lse_max_only(o_parts, lse_parts):
                                     _mut_merge_lse_max_only], ids=lambda f: f.__name__)
 def test_planted_merge_mistake_is_caught(mutant):
     assert _merge_checks(mutant) != []
+
+
+# ---------------------------------------------------------------------------
+# The backward restricted to selected query rows (dQ on sampled rows of very
+# long sequences): row i of dQ depends only on q_i, dO_i and all keys.
+# ---------------------------------------------------------------------------
+
+def _rows_bwd_checks(rows_fn):
+    """rows_fn(q_rows, k, v, dO_rows, scale) -> (dQ_rows, D_rows)."""
+    bad = []
+    # 1. Hand-worked example: dQ = [[3/4 ln 3, 0]].
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked.json")))
+    ln3 = math.log(3.0)
+    dq, _ = rows_fn(np.array([[1.0, 0.0]]), np.array([[0.0, 0.0], [ln3, 0.0]]),
+                    np.array(g["v"]), np.array(g["dO"]), 1.0)
+    if np.abs(dq - np.array([[0.75 * ln3, 0.0]])).max() > 1e-14:
+        bad.append("hand-worked dQ")
+    # 2. torch float64 autograd through its own attention, on a row subset.
+    q = rnd((10, 6), 110); k = rnd((14, 6), 111); v = rnd((14, 5), 112); G = rnd((10, 5), 113)
+    s = 0.41
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None],
+                                                           tv[None, None], scale=s)[0, 0]
+    out.backward(torch.from_numpy(G))
+    rows = [0, 4, 9]
+    dq, D = rows_fn(q[rows], k, v, G[rows], s)
+    if np.abs(dq - tq.grad.numpy()[rows]).max() > 1e-12:
+        bad.append("torch autograd dQ rows")
+    O = out.detach().numpy()
+    if np.abs(D - (G[rows] * O[rows]).sum(1)).max() > 1e-12:
+        bad.append("D = rowsum(dO * O)")
+    # 3. Q = 0 closed form: P uniform, dP_ij = dO_i . v_j, so
+    #    dQ_i = s (1/N) sum_j (dO_i . (v_j - vbar)) k_j.
+    k = rnd((7, 4), 114); v = rnd((7, 3), 115); G = rnd((2, 3), 116)
+    dq, _ = rows_fn(np.zeros((2, 4)), k, v, G, s)
+    ref = s / 7.0 * ((G @ (v - v.mean(0)).T) @ k)
+    if np.abs(dq - ref).max() > 1e-13:
+        bad.append("Q=0 dQ closed form")
+    return bad
+
+
+def test_backward_rows_pins():
+    assert _rows_bwd_checks(A.sdpa_backward_rows) == []
+
+
+def test_backward_rows_match_full_backward():
+    q = rnd((40, 8), 1); k = rnd((33, 8), 2); v = rnd((33, 8), 3); G = rnd((40, 8), 4)
+    r = A.sdpa_backward_head(q, k, v, G, 0.3)
+    rows = [0, 7, 21, 39]
+    dq, D = A.sdpa_backward_rows(q[rows], k, v, G[rows], 0.3)
+    assert np.abs(dq - r["dQ"][rows]).max() <= 1e-14
+    assert np.abs(D - r["D"][rows]).max() <= 1e-14
+
+
+def _mut_rows(change):
+    def f(q, k, v, dO, s):
+        q, k, v, dO = map(np.asarray, (q, k, v, dO))
+        P, _, _ = A.softmax_rows(s * (q @ k.T))
+        D = (dO * (P @ v)).sum(1)
+        dP = dO @ v.T
+        if change == "drop_D":
+            dS = P * dP
+        elif change == "D_of_dO_only":
+            D = dO.sum(1)
+            dS = P * (dP - D[:, None])
+        else:
+            dS = P * (dP - D[:, None])
+        return (dS @ k if change == "no_scale" else s * (dS @ k)), D
+    f.__name__ = change
+    return f
+
+
+@pytest.mark.parametrize("change", ["drop_D", "D_of_dO_only", "no_scale"])
+def test_planted_rows_mistake_is_caught(change):
+    assert _rows_bwd_checks(_mut_rows(change)) != []
+
+
+def _mut_normalised_without_rescale(q, k, v, s, block=8, order=None):
+    # mixes the old output by l_old instead of exp(m - m') * l_old
+    q, k, v = map(np.asarray, (q, k, v))
+    m = np.full(q.shape[0], -np.inf); l = np.zeros(q.shape[0]); O = np.zeros((q.shape[0], v.shape[1]))
+    for a, b in A._blocks(k.shape[0], block, order):
+        Sb = s * q @ k[a:b].T
+        m_new = np.maximum(m, Sb.max(1))
+        Pt = np.exp(Sb - m_new[:, None])
+        w_b = Pt.sum(1)
+        theta = l / (l + w_b)
+        O = theta[:, None] * O + (1.0 - theta)[:, None] * ((Pt @ v[a:b]) / w_b[:, None])
+        l, m = l + w_b, m_new
+    return O, m + np.log(l)
+
+
+def test_planted_normalised_online_mistake_is_caught():
+    assert _fwd_checks(A.sdpa_forward_head,
+                       online_heads=(_mut_normalised_without_rescale,)) != []
