@@ -148,12 +148,20 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
 
 /* ------------------------------------------------------------------------ */
 /* fp32 path: every tensor is float32, 1 <= d <= 128, pointers 4-byte        */
-/* aligned; no rounding anywhere (P and dS stay fp32).  d = 64 and 128 run   */
-/* on the fp32 matrix cores (key and query tiles of 32) when one head of one */
-/* tensor fits 2 GiB; other d use FMA kernels with key blocks of 8 (the 8     */
-/* stacks of 8 of 算珠楼的掌簿人, fable section 二).  Same method and          */
-/* citations as the bf16 calls.                                              */
+/* aligned; no rounding anywhere (P and dS stay fp32).  Same method and      */
+/* citations as the bf16 calls.  The key block (keys per rescale step) is    */
+/* chosen by shape, see fa_f32_key_block: up to N = 256, and for head dims   */
+/* other than 64 and 128, FMA kernels step through key blocks of 8 with the  */
+/* exact running max (the 64 rows in 8 stacks of 8 of 算珠楼的掌簿人, fable   */
+/* section 二, updated by the rule of 账房先生的奔命, section 六); longer      */
+/* sequences at d = 64 or 128 run on the fp32 matrix cores with key and      */
+/* query tiles of 32 (when one head of one tensor fits 2 GiB).               */
 /* ------------------------------------------------------------------------ */
+
+/* Keys per rescale step that fa_fwd_f32 and fa_bwd_f32 use for sequence    */
+/* length N and head dim d: 8 or 32.  -1 if N < 0 or d is outside 1..128.   */
+/* Pure function of its arguments; launches nothing.                        */
+int64_t fa_f32_key_block(int64_t N, int64_t d);
 
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,

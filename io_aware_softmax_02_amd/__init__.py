@@ -22,7 +22,7 @@ from ._lib import LIB, FAError, FA_OK, status_str  # noqa: F401
 
 __all__ = [
     "fa_fwd", "fa_fwd_split_max", "fa_fwd_split", "fa_merge", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
-    "fa_bwd_dq", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
+    "fa_bwd_dq", "fa_f32_key_block", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
     "default_scale", "FAError", "status_str",
 ]
 
@@ -164,8 +164,15 @@ def _parts(o_part, lse_part, n: int, shape) -> None:
 
 def fa_fwd_f32(q, k, v, scale: Optional[float] = None, o=None, lse=None, stream=None
                ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """fp32 forward (key blocks of 8).  Returns (o, lse)."""
+    """fp32 forward.  Returns (o, lse).  Keys per rescale step:
+    fa_f32_key_block(N, d)."""
     return _fwd(LIB.fa_fwd_f32, "fa_fwd_f32", torch.float32, q, k, v, scale, o, lse, stream)
+
+
+def fa_f32_key_block(N: int, d: int) -> int:
+    """Keys per rescale step of the fp32 calls at this shape (8 or 32; -1
+    for an invalid shape)."""
+    return int(LIB.fa_f32_key_block(N, d))
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

@@ -31,6 +31,7 @@ PROTOTYPES = {
     "fa_bwd_preprocess": (_st, [_p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "fa_bwd_dkdv": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
     "fa_bwd_dq": (_st, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
+    "fa_f32_key_block": (_i64, [_i64, _i64]),
     "fa_fwd_f32": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
     "fa_bwd_f32_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fa_bwd_f32": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,

@@ -22,6 +22,7 @@ int launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* o_
                           int nsplit, hipStream_t stream);
 int launch_merge_bf16(const float* o_part, const float* lse_part, int nsplit, int64_t rows,
                       int64_t d, void* o, float* lse, hipStream_t stream);
+int f32_key_block(int64_t N, int64_t d);
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
 int launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
@@ -210,6 +211,11 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
   FA_TRY(check_fwd(q, k, v, o, lse, s, scale, false));
   if (s.empty()) return FA_OK;
   return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
+}
+
+int64_t fa_f32_key_block(int64_t N, int64_t d) {
+  if (N < 0 || d < 1 || d > 128) return -1;
+  return fa::f32_key_block(N, d);
 }
 
 size_t fa_bwd_f32_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {

@@ -439,8 +439,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // K and V tiles are in row-segment order (lds_tile.h): K is read along rows
 // for S^T and with transposing reads for K^T, V along rows only, and the
 // tiles' swizzle keeps both kinds of read free of bank conflicts.  Keys past
-// N read as zero rows
-// of K and V, so their dS multiplies a zero row of K^T and adds nothing to dQ.
+// N read as zero rows of K and V and their scores are set to -inf, so their
+// P and dS are 0.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
@@ -566,6 +566,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
           }
         }
         __builtin_amdgcn_s_setprio(0);
+      }
+      // Keys past N in the last tile read as zero rows of K and V; their P
+      // would be 2^(-LSE log2 e), which overflows when every score of the
+      // row is below about -88.  They do not exist: their scores are -inf,
+      // so P and dS are 0.
+      const int key0 = it * C::BK + kb2 * 32;
+      if (key0 + 32 > N) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 16 * h + 4 * g + i >= N) s[qb][h][i] = -INFINITY;
       }
       bf16x8 sb[2];
 #pragma unroll

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
 
 }  // namespace
 
-bool f32_mfma_ok(int64_t N, int64_t d);
+bool f32_mfma_fits(int64_t N, int64_t d);
 int launch_fwd_f32_mfma(const float* q, const float* k, const float* v, float* o, float* lse,
                         int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
 
@@ -244,10 +244,21 @@ int launch_bwd_f32_mfma(const float* q, const float* k, const float* v, const fl
                         const float* dO, const float* delta, float* dq, float* dk, float* dv,
                         int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream);
 
+// Keys per rescale step of the fp32 calls.  Up to kSmallN keys (the fable's
+// 64 rows among them) and for head dims the matrix cores do not take, the
+// kernels of this file step through blocks of 8 with the exact running max;
+// longer sequences at d = 64 or 128 run on the fp32 matrix cores with blocks
+// of 32.  Both are exact in real arithmetic; at the small sizes the
+// matrix cores would not pay (a few workgroups, launch-bound either way).
+constexpr int64_t kSmallN = 256;
+int f32_key_block(int64_t N, int64_t d) {
+  return (N > kSmallN && f32_mfma_fits(N, d)) ? 32 : T;
+}
+
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
-  // d = 64, 128: matrix-core kernel (attn_f32_mfma.hip); other d: this file's.
-  if (f32_mfma_ok(N, d)) return launch_fwd_f32_mfma(q, k, v, o, lse, BH, N, d, scale, stream);
+  if (f32_key_block(N, d) != T)
+    return launch_fwd_f32_mfma(q, k, v, o, lse, BH, N, d, scale, stream);
   const int ntq = (int)((N + T - 1) / T);
   hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)(ntq * BH)), dim3(64), 0, stream, q, k, v,
                      o, lse, (int)N, (int)d, ntq, scale);
@@ -263,7 +274,7 @@ int launch_bwd_f32(const float* q, const float* k, const float* v, const float* 
                      stream, o, dO, delta, rows, (int)d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  if (f32_mfma_ok(N, d))
+  if (f32_key_block(N, d) != T)
     return launch_bwd_f32_mfma(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, d, scale, stream);
   const int nt = (int)((N + T - 1) / T);
   hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k,

@@ -454,6 +454,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_mfma_kernel(
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(fmaf(s[i], c2, -lse2)) * (dp[i] - dl);
+    // Keys past N in the last tile read as zero rows of K and V; their P
+    // would be 2^(-LSE log2 e), which overflows when every score of the row
+    // is below about -88.  They do not exist, so their dS is 0.
+    if (j * C::BT + C::BT > N) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (j * C::BT + 8 * (i >> 2) + 4 * g + (i & 3) >= N) ds[i] = 0.0f;
+    }
     const float* kc = Kt + 4 * g * C::S + li;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -511,9 +519,9 @@ int launch_bwd_f32_mfma(const float* q, const float* k, const float* v, const fl
                   : launch_bwd<64>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
 }
 
-// Whether the matrix-core fp32 kernels take this shape: d of 64 or 128 and
-// one head of one tensor (plus a tile past the end) within 32-bit offsets.
-bool f32_mfma_ok(int64_t N, int64_t d) {
+// Whether the matrix-core fp32 kernels can take this shape: d of 64 or 128
+// and one head of one tensor (plus a tile past the end) within 32-bit offsets.
+bool f32_mfma_fits(int64_t N, int64_t d) {
   return (d == 64 || d == 128) && (N + 64) * d * 4 < (int64_t(1) << 31);
 }
 

@@ -243,3 +243,18 @@ int main() {
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_f32_key_block(lib):
+    # The 64-row example of the fable (8 stacks of 8) runs blocks of 8; long
+    # sequences at d = 64 / 128 run the 32-key matrix-core tiles; other head
+    # dims always blocks of 8; invalid arguments -1.
+    assert lib.fa_f32_key_block(64, 64) == 8
+    assert lib.fa_f32_key_block(256, 128) == 8
+    assert lib.fa_f32_key_block(257, 128) == 32
+    assert lib.fa_f32_key_block(4096, 64) == 32
+    assert lib.fa_f32_key_block(4096, 17) == 8
+    assert lib.fa_f32_key_block(0, 64) == 8
+    assert lib.fa_f32_key_block(-1, 64) == -1
+    assert lib.fa_f32_key_block(64, 0) == -1
+    assert lib.fa_f32_key_block(64, 129) == -1
