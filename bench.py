@@ -176,27 +176,69 @@ def cpu_configs(args):
     del np
 
 
+def host_cores():
+    """Host cores this process may run on (its CPU affinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _limit_blas(threads):
+    """Pool initializer: this worker's BLAS uses `threads` threads."""
+    global _BLAS_LIMIT
+    from threadpoolctl import threadpool_limits
+    _BLAS_LIMIT = threadpool_limits(limits=threads)
+
+
+def _oracle_head(args):
+    """One head of the oracle, forward then backward (a pool task)."""
+    import oracle
+    q, k, v, g, scale = args
+    oracle.sdpa_forward_head(q, k, v, scale)
+    oracle.sdpa_backward_head(q, k, v, g, scale)
+    return True
+
+
+# Host memory one worker needs for a head of B=1, H=16, N=8192, d=128
+# (S, P, dP and dS are 537 MB each in float64, plus temporaries).
+CPU_BYTES_PER_WORKER = 3.5e9
+
+
 def cpu_baseline(w, heads):
     """The fp64 oracle (forward + backward, materialising S and P) on `heads`
-    of the workload's heads; returns a dict in the metric's unit."""
-    import numpy as np
-    import oracle
+    of the workload's heads, spread over a process pool (one head per task,
+    the BLAS threads of each worker = cores / workers, since the oracle's
+    elementwise exp runs on one thread); returns a dict in the metric's
+    unit.  The workers are started and warmed before the clock starts."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
     import synth
-    threads = blas_threads()
+    cores = host_cores()
+    try:
+        avail = os.sysconf("SC_AVPHYS_PAGES") * os.sysconf("SC_PAGE_SIZE")
+    except (ValueError, OSError):  # pragma: no cover
+        avail = 16e9
+    workers = max(1, min(cores, heads, int(avail * 0.6 // CPU_BYTES_PER_WORKER)))
+    per = max(1, cores // workers)
     q, k, v, dO = synth.make_inputs(w)
-    sel = list(range(heads))
     f64 = synth.to_f64
-    qf, kf, vf, gf = (f64(x)[:, :heads] for x in (q, k, v, dO))
-    t0 = time.perf_counter()
-    oracle.sdpa_forward(qf, kf, vf, w.scale)
-    oracle.sdpa_backward(qf, kf, vf, gf, w.scale)
-    dt = time.perf_counter() - t0
+    qf, kf, vf, gf = (f64(x).reshape(w.B * w.H, w.N, w.d)[:heads] for x in (q, k, v, dO))
+    tasks = [(qf[h], kf[h], vf[h], gf[h], w.scale) for h in range(heads)]
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_limit_blas,
+                                initargs=(per,)) as ex:
+        tiny = [(x[:64], y[:64], z[:64], g[:64], w.scale) for x, y, z, g, _ in tasks[:workers]]
+        list(ex.map(_oracle_head, tiny))          # workers started, modules imported
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_head, tasks))
+        dt = time.perf_counter() - t0
     flops = (w.fwd_flops() + w.bwd_flops()) * heads / (w.B * w.H)
-    del np, sel
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers * per),
             "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of B={w.B},H={w.H},N={w.N},d={w.d}, "
-                      f"forward+backward, float64 numpy, {dt:.1f} s"}
+                      f"forward+backward, float64 numpy, process pool of {workers} workers x "
+                      f"{per} BLAS threads ({cores} cores in the affinity set), {dt:.1f} s"}
 
 
 def settle(seconds, dev):
@@ -228,8 +270,8 @@ def sweep(args):
     stream = torch.cuda.current_stream(dev)
     B, H, d = 1, 16, 128
     for N in (2048, 4096, 8192, 16384, 32768, 65536, 131072):
-        q, k, v, dO = (x.to(dev) for x in synth.make_qkv(B, H, N, d, torch.bfloat16, seed=N,
-                                                        backward=True))
+        # the same inputs the long-sequence parity tests check
+        q, k, v, dO = (x.to(dev) for x in synth.sweep_inputs(N))
         s = synth.default_scale(d)
         o = torch.empty_like(q)
         lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
@@ -392,6 +434,30 @@ def fp32(args):
         del q, k, v, dO, o, lse, dq, dk, dv, ws
 
 
+def standard_attention(q, k, v, scale, S=None, P=None, O=None):
+    """Standard attention in three steps through device memory (the
+    three-line form of 账房先生的奔命, section 五), for contrast with the
+    tiled kernel only; no part of the library.  S = (scale Q) K^T is written
+    as an N x N bf16 matrix per head, P = softmax(S) is read and written again,
+    O = P V.  torch's own GEMM and softmax kernels do the work.  Returns
+    (S, P, O); preallocated S, P, O are filled in place."""
+    import torch
+    B, H, N, d = q.shape
+    # The right operand of a batched bf16 product is made contiguous first.
+    kt = k.transpose(-1, -2).contiguous()
+    qs = q * scale
+    if S is None:
+        S = torch.empty(B, H, N, N, dtype=q.dtype, device=q.device)
+    if P is None:
+        P = torch.empty_like(S)
+    if O is None:
+        O = torch.empty_like(q)
+    torch.matmul(qs, kt, out=S)
+    torch.softmax(S, dim=-1, out=P)
+    torch.matmul(P, v, out=O)
+    return S, P, O
+
+
 def contrast(args):
     """Standard attention as three steps through device memory, for contrast
     with the tiled kernel (no part of the library): S = (s Q) K^T written as an
@@ -420,9 +486,7 @@ def contrast(args):
         # The right operand of a batched bf16 product is made contiguous first.
         kt = k.transpose(-1, -2).contiguous()
         qs = q * sc
-        S = torch.empty(B, H, N, N, dtype=torch.bfloat16, device=dev)
-        P = torch.empty_like(S)
-        O = torch.empty_like(q)
+        S, P, O = standard_attention(q, k, v, sc)
         step_s = lambda: torch.matmul(qs, kt, out=S)
         step_p = lambda: torch.softmax(S, dim=-1, out=P)
         step_o = lambda: torch.matmul(P, v, out=O)
@@ -437,9 +501,7 @@ def contrast(args):
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
-        S2 = torch.matmul(qs, kt)
-        P2 = torch.softmax(S2, dim=-1)
-        O2 = torch.matmul(P2, v)
+        S2, P2, O2 = standard_attention(q, k, v, sc)
         torch.cuda.synchronize()
         peak_std = torch.cuda.max_memory_allocated() - base
         del S2, P2
@@ -494,6 +556,10 @@ def main():
     import synth
 
     w = synth.WORKLOADS[WORKLOAD]
+    # The CPU baseline runs first, while this process has not yet touched the
+    # GPU, so that its worker processes start from a process without a GPU
+    # context; the pool is shut down before the GPU work begins.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_heads)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q, k, v, dO = (x.to(dev) for x in synth.make_inputs(w))
@@ -518,15 +584,20 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     mem_base = torch.cuda.memory_allocated()
 
-    def fwd():
-        fa.fa_fwd(q, k, v, s, o=o, lse=lse)
-
-    def bwd():
-        fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+    # One step is the whole path: the forward, then the backward's three
+    # launches (fa_bwd runs exactly fa_bwd_preprocess, fa_bwd_dkdv and
+    # fa_bwd_dq in this order; they are called one by one here so that an
+    # event can be recorded between them).
+    stages = (
+        ("fwd_bf16", lambda: fa.fa_fwd(q, k, v, s, o=o, lse=lse)),
+        ("bwd_pre_bf16", lambda: fa.fa_bwd_preprocess(o, dO, delta)),
+        ("bwd_dkdv_bf16", lambda: fa.fa_bwd_dkdv(q, k, v, lse, dO, delta, s, dk=dk, dv=dv)),
+        ("bwd_dq_bf16", lambda: fa.fa_bwd_dq(q, k, v, lse, dO, delta, s, dq=dq)),
+    )
 
     def step():
-        fwd()
-        bwd()
+        for _, fn in stages:
+            fn()
 
     # The shader clock ramps up over the first ~30 ms of work after idle
     # (per-launch trace durations fall by 20% over the first 15 launches);
@@ -540,32 +611,39 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # fa_bwd itself gives the same gradients as its three stages
+    ref = (dq.clone(), dk.clone(), dv.clone())
+    fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(ref, (dq, dk, dv)))
+    del ref
 
-    # Timed region: exactly K steps, synchronised on both sides.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # Timed region: exactly K steps, synchronised on both sides.  Events are
+    # chained on the launch stream, one after every launch: the interval
+    # before launch i of step t ends where the next begins, so the
+    # per-kernel averages add up to the time per step.
+    ns = len(stages)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(ns * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
+    ev[0].record(stream)
+    for t in range(args.steps):
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[t * ns + i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_total = ev[0].elapsed_time(ev[-1])
+    ms_step = ms_total / args.steps
+    per_kernel = {name: sum(ev[t * ns + i].elapsed_time(ev[t * ns + i + 1])
+                            for t in range(args.steps)) / args.steps
+                  for i, (name, _) in enumerate(stages)}
+    step_times = sorted(ev[t * ns].elapsed_time(ev[(t + 1) * ns]) for t in range(args.steps))
     peak_mem = torch.cuda.max_memory_allocated()
-    # Per-step spread (after the timed region): median and minimum of single steps.
-    per_step = sorted(time_launches(step, 1, stream) for _ in range(max(args.steps, 5)))
-
-    # Per-kernel launch times (each entry point launches one kernel except
-    # fa_bwd, whose three stages are timed through their own entry points).
-    n = max(args.steps, 5)
-    ms_fwd = time_launches(fwd, n, stream)
-    ms_pre = time_launches(lambda: fa.fa_bwd_preprocess(o, dO, delta), n, stream)
-    ms_dkdv = time_launches(lambda: fa.fa_bwd_dkdv(q, k, v, lse, dO, delta, s, dk=dk, dv=dv),
-                            n, stream)
-    ms_dq = time_launches(lambda: fa.fa_bwd_dq(q, k, v, lse, dO, delta, s, dq=dq), n, stream)
-    ms_bwd = time_launches(bwd, n, stream)
+    ms_fwd = per_kernel["fwd_bf16"]
+    ms_pre, ms_dkdv, ms_dq = (per_kernel[x] for x in ("bwd_pre_bf16", "bwd_dkdv_bf16",
+                                                      "bwd_dq_bf16"))
+    ms_bwd = ms_pre + ms_dkdv + ms_dq
 
     # Same-box reference for the matrix-core rate attainable on this kind of
     # data (outside the timed region): one 8192^3 bf16 GEMM through torch
@@ -608,8 +686,8 @@ def main():
         "warmup": args.warmup,
         "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
-        "ms_per_step_min": round(per_step[0], 4),
+        "ms_per_step_median": round(step_times[len(step_times) // 2], 4),
+        "ms_per_step_min": round(step_times[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -626,6 +704,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "kernels": {kname: {"ms": round(kv["ms"], 4), "tflops": round(kv["tflops"], 2)}
                     for kname, kv in kernels.items()},
+        "kernels_timing": "average per launch over the timed steps (events between launches)",
         "hbm_copy_GBps": round(2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9, 1),
         "reference_gemm": {"what": "torch.matmul bf16 8192x8192x8192, N(0,1) operands",
                            "tflops": round(gemm_tf, 1),
@@ -638,8 +717,8 @@ def main():
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom), "traffic_unit": "HBM bytes per launch"},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -128,19 +128,31 @@ def make_parts(P: int, B: int, H: int, N: int, d: int, seed: int, dead_every: in
 
 
 def sampled_rows(w: Workload) -> np.ndarray:
-    """Query rows checked per head for the very long workload.
+    """Query rows checked per head for the very long workload
+    (``draw_rows`` with the workload's sizes and seed)."""
+    assert w.sample_rows is not None
+    return draw_rows(w.N, w.B * w.H, w.sample_rows, w.seed)
 
-    Per head: rows 0 and N-1 plus (sample_rows - 2) rows drawn without
-    replacement from the rest with ``np.random.default_rng(seed)``; the heads
-    draw in order.  Returns an int64 array [B*H, sample_rows], sorted per head.
+
+def draw_rows(N: int, heads: int, count: int, seed: int) -> np.ndarray:
+    """Query rows checked one by one at sizes the oracle cannot run in full.
+
+    Per head: rows 0 and N-1 plus (count - 2) rows drawn without replacement
+    from the rest with ``np.random.default_rng(seed)``; the heads draw in
+    order.  Returns an int64 array [heads, count], sorted per head.
     """
-    assert w.sample_rows is not None and w.sample_rows >= 2
-    rng = np.random.default_rng(w.seed)
-    out = np.empty((w.B * w.H, w.sample_rows), dtype=np.int64)
-    for bh in range(w.B * w.H):
-        rest = rng.choice(np.arange(1, w.N - 1), size=w.sample_rows - 2, replace=False)
-        out[bh] = np.sort(np.concatenate([[0, w.N - 1], rest]))
+    assert count >= 2 and N >= count
+    rng = np.random.default_rng(seed)
+    out = np.empty((heads, count), dtype=np.int64)
+    for bh in range(heads):
+        rest = rng.choice(np.arange(1, N - 1), size=count - 2, replace=False)
+        out[bh] = np.sort(np.concatenate([[0, N - 1], rest]))
     return out
+
+
+def sweep_inputs(N: int, backward: bool = True):
+    """Inputs of the sequence-length sweep: B=1, H=16, d=128, bf16, seed N."""
+    return make_qkv(1, 16, N, 128, torch.bfloat16, seed=N, backward=backward)
 
 
 def to_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:

@@ -72,8 +72,10 @@ def grad_err(x, ref):
 # ---------------------------------------------------------------------------
 
 def test_tiny_f32_forward():
+    """64 rows in 8 key blocks of 8: eight rescale steps with the running max."""
     w = synth.WORKLOADS["tiny_f32_n64_d64"]
     say(f"case {w.name}")
+    assert fa.fa_f32_key_block(w.N, w.d) == w.block == 8
     q, k, v, _ = synth.make_inputs(w)
     O, L = fa.fa_fwd_f32(gpu(q), gpu(k), gpu(v), w.scale)
     torch.cuda.synchronize()
@@ -83,8 +85,8 @@ def test_tiny_f32_forward():
     assert ea <= TOL_F32 and el <= TOL_F32
 
 
-# d = 64 and 128 run on the fp32 matrix-core kernels; the other head dims on
-# the FMA kernels.
+# Up to N = 256 and for d outside {64, 128} the FMA kernels run (key blocks
+# of 8); longer sequences at d = 64 and 128 the fp32 matrix-core kernels.
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 1), (1, 2, 7, 3), (2, 1, 65, 64),
                                      (1, 1, 100, 128), (1, 3, 33, 17), (1, 1, 9, 8),
                                      (1, 1, 1, 128), (1, 2, 1000, 128), (2, 2, 513, 64),
@@ -295,6 +297,70 @@ def test_bf16_nondefault_scale(d, scale):
         e = grad_err(f64(x), ref)
         say(f"  {name} err {e:.3e}")
         assert e <= TOL_BF16_GRAD_REL, name
+
+
+NEG_SCALE = 2.0
+
+
+def anti_aligned(N, d, dtype, seed):
+    """Q and K pointing opposite ways along e_0: q_i = (16, n_i / 8),
+    k_j = (-4, m_j) with n, m iid N(0,1) (all exact in bf16).  At scale 2
+    every score is -128 +- 3, so every LSE is below -100 and exp(-LSE)
+    overflows fp32, while the keys' common component (4 against unit noise)
+    keeps dQ well conditioned."""
+    q, k, v, dO = synth.make_qkv(1, 2, N, d, dtype, seed=seed, backward=True)
+    q[..., 1:] *= 0.125
+    q[..., 0] = 16.0
+    k[..., 0] = -4.0
+    return q, k, v, dO
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [65, 1000])
+def test_bf16_ragged_very_negative_lse(N, d):
+    """Ragged last key tile with every LSE below -100: keys past N must not
+    enter dQ (their zero rows would give P = exp(-LSE) = inf)."""
+    say(f"case bf16 ragged, LSE < -100, N={N} d={d}")
+    q, k, v, dO = anti_aligned(N, d, torch.bfloat16, 800 + N + d)
+    O, L, dq, dk, dv = run_bf16_fwd_bwd(q, k, v, dO, NEG_SCALE)
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), NEG_SCALE)
+    say(f"  LSE range [{Lref.min():.1f}, {Lref.max():.1f}]")
+    assert Lref.max() < -100.0
+    check_fwd_bf16(O, L, Oref, Lref, f"  fwd N={N} d={d}")
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), NEG_SCALE)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert torch.isfinite(x).all(), name
+        e = grad_err(f64(x), ref)
+        say(f"  {name} err {e:.3e}")
+        assert e <= TOL_BF16_GRAD_REL, name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [65, 300, 1000])
+def test_f32_ragged_very_negative_lse(N, d):
+    """The same on the fp32 path (N = 65: key blocks of 8; 300, 1000: the
+    32-key matrix-core tiles).  fp32 forms a score of size |S| with an
+    absolute error of order |S| 2^-24 sqrt(d), so here (|S| ~ 130) the
+    stated 1e-5 bounds apply relative to max |S|."""
+    say(f"case f32 ragged, LSE < -100, N={N} d={d} (key block {fa.fa_f32_key_block(N, d)})")
+    q, k, v, dO = anti_aligned(N, d, torch.float32, 900 + N + d)
+    qg, kg, vg, gg = gpu(q), gpu(k), gpu(v), gpu(dO)
+    O, L = fa.fa_fwd_f32(qg, kg, vg, NEG_SCALE)
+    dq, dk, dv = fa.fa_bwd_f32(qg, kg, vg, O, L, gg, NEG_SCALE)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.sdpa_forward(f64(q), f64(k), f64(v), NEG_SCALE)
+    assert Lref.max() < -100.0
+    smax = float(np.abs(NEG_SCALE * np.einsum("bhid,bhjd->bhij", f64(q), f64(k))).max())
+    tol = TOL_F32 * smax
+    eo, el = max_abs(f64(O), Oref), max_abs(f64(L), Lref)
+    say(f"  max |S| {smax:.1f}: O max-abs {eo:.2e}, LSE max-abs {el:.2e} (bound {tol:.2e})")
+    assert eo <= tol and el <= tol
+    rq, rk, rv, _ = oracle.sdpa_backward(f64(q), f64(k), f64(v), f64(dO), NEG_SCALE)
+    for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert torch.isfinite(x).all(), name
+        e = grad_err(f64(x), ref)
+        say(f"  {name} rel-Frobenius {e:.2e}")
+        assert e <= tol, name
 
 
 @pytest.mark.parametrize("d", [64, 128])
