@@ -52,7 +52,8 @@ typedef enum fa_status {
   FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
   FA_ERR_SCALE = 6,       /* scale not finite or not > 0                       */
   FA_ERR_ALIAS = 7,       /* an output overlaps an input or another output     */
-  FA_ERR_HIP = 8          /* the HIP runtime rejected a launch                 */
+  FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                 */
+  FA_ERR_SCRATCH = 9      /* problem larger than a fixed scratch array         */
 } fa_status;
 
 /* A hipStream_t, passed as an opaque pointer so this header needs no HIP. */
@@ -127,6 +128,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                  fa_stream_t stream);
+
+/* fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same computation, arguments and errors as fa_bwd, without the workspace
+ * arguments.  Its workspace (D, one fp32 per query row) is a fixed array the
+ * library holds on every GPU it runs on, FA_BWD_NOALLOC_MAX_ROWS rows
+ * (16 MiB); B*H*N above that is FA_ERR_SCRATCH.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's array once.  Every call on one GPU uses the same
+ * array: calls that overlap in time on one GPU (different streams, or other
+ * threads) race and give wrong gradients; calls ordered on one stream do not.
+ * Results are bit-identical to fa_bwd. */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                         fa_stream_t stream);
 
 /* The three stages of fa_bwd, exposed so that each launch can be timed and
  * tested on its own.  `delta` is [B][H][N] fp32 (16-byte aligned).

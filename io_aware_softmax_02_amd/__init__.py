@@ -18,10 +18,10 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-from ._lib import LIB, FAError, FA_OK, status_str  # noqa: F401
+from ._lib import LIB, FAError, FA_OK, FA_BWD_NOALLOC_MAX_ROWS, status_str  # noqa: F401
 
 __all__ = [
-    "fa_fwd", "fa_fwd_split_max", "fa_fwd_split", "fa_merge", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
+    "fa_fwd", "fa_fwd_split_max", "fa_fwd_split", "fa_merge", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
     "fa_bwd_dq", "fa_f32_key_block", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
     "default_scale", "FAError", "status_str",
 ]
@@ -215,6 +215,34 @@ def fa_bwd(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=None,
     """bf16 backward with recomputation.  Returns (dq, dk, dv)."""
     return _bwd(LIB.fa_bwd, LIB.fa_bwd_workspace_bytes, "fa_bwd", torch.bfloat16, q, k, v, o,
                 lse, dO, scale, dq, dk, dv, workspace, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=None,
+                   dv=None, stream=None):
+    """bf16 backward whose workspace is the library's fixed device array
+    (B*H*N <= FA_BWD_NOALLOC_MAX_ROWS); the C call allocates nothing.  Pass
+    dq, dk, dv to make this call allocate nothing either.  Calls that overlap
+    in time on one GPU race.  Returns (dq, dk, dv)."""
+    shape = _shape4(q, "q", torch.bfloat16)
+    for x, name in ((k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
+        _same(shape, x, name, torch.bfloat16)
+    _rows(lse, "lse", shape)
+    B, H, N, d = shape
+    if scale is None:
+        scale = default_scale(d)
+    outs = []
+    for x, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if x is None:
+            x = torch.empty_like(q)
+        else:
+            _same(shape, x, name, torch.bfloat16)
+        outs.append(x)
+    dq, dk, dv = outs
+    with torch.cuda.device(q.device):
+        _check(LIB.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                                  _stream(q.device, stream)), "fa_bwd_noalloc")
+    return dq, dk, dv
 
 
 def fa_bwd_f32(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=None, dv=None,

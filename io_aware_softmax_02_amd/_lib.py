@@ -28,6 +28,8 @@ PROTOTYPES = {
     "fa_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fa_bwd": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
                      _i64, _i64, _i64, _i64, _f, _p]),
+    "fa_bwd_noalloc": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _p,
+                             _i64, _i64, _i64, _i64, _f, _p]),
     "fa_bwd_preprocess": (_st, [_p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "fa_bwd_dkdv": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
     "fa_bwd_dq": (_st, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p]),
@@ -64,6 +66,8 @@ FA_ERR_WORKSPACE = 5
 FA_ERR_SCALE = 6
 FA_ERR_ALIAS = 7
 FA_ERR_HIP = 8
+FA_ERR_SCRATCH = 9
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 22
 
 
 class FAError(RuntimeError):

@@ -2,8 +2,17 @@
 // then launches on the caller's stream.  Nothing is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "validate.h"
+
+// Scratch of fa_bwd_noalloc: D = rowsum(dO * O), one fp32 per query row, for
+// at most FA_BWD_NOALLOC_MAX_ROWS rows (16 MiB).  Every GPU the library runs
+// on holds its own copy from the time the code object is loaded until the
+// process ends.  In host code this name is only a handle for
+// hipGetSymbolAddress: the device address comes from that call, per device.
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
 
 namespace fa {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -77,6 +86,29 @@ fa_status check_bwd(const void* q, const void* k, const void* v, const void* o,
                          {{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {ws, wsz}});
 }
 
+// Device address of `scratch` on device `dev`, looked up once per device
+// with that device current (each device holds the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status scratch_on(int dev, float** out) {
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +124,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: B*H*N exceeds the fixed scratch of fa_bwd_noalloc (FA_BWD_NOALLOC_MAX_ROWS rows)";
   }
   return "unknown fa_status";
 }
@@ -199,6 +232,37 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (s.empty()) return FA_OK;
   float* delta = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
+  FA_TRY(from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, st)));
+  FA_TRY(from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, st)));
+  return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale, st));
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                         fa_stream_t stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(fa::check_shape(s, true));
+  FA_TRY(fa::check_scale(scale));
+  if (s.empty()) return FA_OK;
+  if (s.rows() > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  FA_TRY(fa::check_ptrs({q, k, v, o, dO, dq, dk, dv, lse}, 16));
+  const Sizes z = sizes(s, 2);
+  FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {o, z.tensor},
+                          {lse, z.rows}, {dO, z.tensor}},
+                         {{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}}));
+  hipStream_t st = as_stream(stream);
+  int dev = -1;
+  if (st == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  } else if (hipStreamGetDevice(st, &dev) != hipSuccess) {
+    return FA_ERR_HIP;
+  }
+  float* delta = nullptr;
+  FA_TRY(scratch_on(dev, &delta));
+  // Rows [0, B*H*N) of the scratch are written by the preprocess kernel
+  // before the other two read them (in stream order); nothing needs to start
+  // at zero.
   FA_TRY(from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, st)));
   FA_TRY(from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, st)));
   return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale, st));

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     from io_aware_softmax_02_amd import _lib as L
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = lib.fa_status_str(code).decode()
         assert s and "unknown" not in s
     assert "unknown" in lib.fa_status_str(99).decode()
@@ -258,3 +258,24 @@ def test_f32_key_block(lib):
     assert lib.fa_f32_key_block(-1, 64) == -1
     assert lib.fa_f32_key_block(64, 0) == -1
     assert lib.fa_f32_key_block(64, 129) == -1
+
+
+def test_bwd_noalloc_argument_checks(lib):
+    from io_aware_softmax_02_amd import _lib as L
+
+    def call(ptrs=None, B=1, H=1, N=64, d=64, scale=0.125):
+        q, k, v, o, lse, dO, dq, dk, dv = ptrs if ptrs is not None else P[:9]
+        return lib.fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, None)
+
+    # a problem beyond the fixed array is refused before anything else runs
+    assert call(H=2, N=L.FA_BWD_NOALLOC_MAX_ROWS // 2 + 1, d=128) == L.FA_ERR_SCRATCH
+    assert "FA_ERR_SCRATCH" in lib.fa_status_str(L.FA_ERR_SCRATCH).decode()
+    ptrs = list(P[:9])
+    ptrs[3] = 0
+    assert call(ptrs=ptrs) == L.FA_ERR_NULL
+    ptrs = list(P[:9])
+    ptrs[7] = P[0]                 # dk == q
+    assert call(ptrs=ptrs) == L.FA_ERR_ALIAS
+    assert call(d=96) == L.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == L.FA_ERR_SCALE
+    assert call(ptrs=[0] * 9, N=0) == L.FA_OK
