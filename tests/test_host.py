@@ -84,3 +84,16 @@ def test_cpu_markdown_labels_extrapolation(tmp_path):
     rows = [r for r in md.splitlines() if r.startswith("| `")]
     assert rows == ["| `a` | 1, 2, 8, 4 | 1 of 2 heads, forward | 1.5 | 0.2500 | 3.0 |",
                     "| `b` | 1, 1, 9, 4 | 2 sampled query rows | 0.5 | 0.1250 | 2.25 |"]
+
+
+def test_traffic_calibration_uses_only_the_large_copy(tmp_path):
+    # Copies of tensors a few tens of MB large share the calibration copy's
+    # grid; only dispatches near the largest value calibrate.
+    from io_aware_softmax_02_amd.profile_summary import calibration
+    rows = ["Dispatch_Id,Grid_Size,Kernel_Name,Counter_Name,Counter_Value"]
+    for d, v in ((2, 262160.0), (3, 262156.0), (10, 16400.0), (11, 16399.0), (19, 1.5)):
+        rows.append(f'{d},131072,"__amd_rocclr_copyBuffer",FETCH_SIZE,{v}')
+    rows.append('5,262144,"fa::fwd_bf16_kernel<128>(...)",FETCH_SIZE,49232.0')
+    p = tmp_path / "c.csv"
+    p.write_text("\n".join(rows) + "\n")
+    assert calibration(str(p), "FETCH_SIZE") == 262158.0
