@@ -599,9 +599,24 @@ def main():
         for _, fn in stages:
             fn()
 
+    # fa_bwd itself gives the same gradients as its three stages (checked
+    # before the clock is brought up: the host waits here).
+    step()
+    ref = (dq.clone(), dk.clone(), dv.clone())
+    fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(ref, (dq, dk, dv)))
+    del ref
+    # Events of the timed region, chained on the launch stream, one after
+    # every launch: the interval before launch i of step t ends where the
+    # next begins, so the per-kernel averages add up to the time per step.
+    ns = len(stages)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(ns * args.steps + 1)]
+
     # The shader clock ramps up over the first ~30 ms of work after idle
-    # (per-launch trace durations fall by 20% over the first 15 launches);
-    # untimed steps for `settle` seconds bring it to its working level.
+    # (per-launch durations fall by 20% over the first 15 launches); untimed
+    # steps for `settle` seconds bring it to its working level, and the
+    # warm-up steps run straight into the timed ones.
     t_settle = time.perf_counter()
     settle_steps = 0
     while time.perf_counter() - t_settle < args.settle:
@@ -610,20 +625,8 @@ def main():
         settle_steps += 1
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    # fa_bwd itself gives the same gradients as its three stages
-    ref = (dq.clone(), dk.clone(), dv.clone())
-    fa.fa_bwd(q, k, v, o, lse, dO, s, dq=dq, dk=dk, dv=dv, workspace=ws)
-    torch.cuda.synchronize()
-    assert all(torch.equal(x, y) for x, y in zip(ref, (dq, dk, dv)))
-    del ref
 
-    # Timed region: exactly K steps, synchronised on both sides.  Events are
-    # chained on the launch stream, one after every launch: the interval
-    # before launch i of step t ends where the next begins, so the
-    # per-kernel averages add up to the time per step.
-    ns = len(stages)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(ns * args.steps + 1)]
+    # Timed region: exactly K steps, synchronised on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
