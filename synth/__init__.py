@@ -97,13 +97,18 @@ def make_inputs(w: Workload, backward: Optional[bool] = None):
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
              backward: bool = False, outlier_row: Optional[int] = None,
-             outlier_factor: float = 8.0):
-    g = torch.Generator().manual_seed(seed)
+             outlier_factor: float = 8.0, device: Optional[torch.device] = None):
+    """Seeded iid N(0,1) tensors, drawn on the CPU (the recipe above), or
+    with ``device`` given, by that device's own generator seeded the same way
+    (other values, same distribution; for sizes whose CPU draw would take
+    long)."""
+    g = torch.Generator(device=device or "cpu").manual_seed(seed)
     shape = (B, H, N, d)
-    q = torch.randn(shape, generator=g).to(dtype)
-    k = torch.randn(shape, generator=g).to(dtype)
-    v = torch.randn(shape, generator=g).to(dtype)
-    dO = torch.randn(shape, generator=g).to(dtype) if backward else None
+    dev = {} if device is None else {"device": device}
+    q = torch.randn(shape, generator=g, **dev).to(dtype)
+    k = torch.randn(shape, generator=g, **dev).to(dtype)
+    v = torch.randn(shape, generator=g, **dev).to(dtype)
+    dO = torch.randn(shape, generator=g, **dev).to(dtype) if backward else None
     if outlier_row is not None:
         k[:, :, outlier_row, :] *= outlier_factor
     return q, k, v, dO

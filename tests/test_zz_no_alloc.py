@@ -81,3 +81,26 @@ def test_noalloc_refuses_problems_beyond_its_scratch():
     assert st == FA_ERR_SCRATCH
     assert "FA_ERR_SCRATCH" in fa.status_str(st)
     torch.cuda.synchronize()
+
+
+def test_noalloc_at_its_maximum_rows():
+    """B*H*N equal to the scratch array's size (2^22 rows): bit-identical to
+    fa_bwd, and the call allocates nothing."""
+    B, H, N, d = 4, 64, 16384, 128
+    assert B * H * N == FA_BWD_NOALLOC_MAX_ROWS
+    print(f"case fa_bwd_noalloc at its maximum: B={B} H={H} N={N} d={d}", flush=True)
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=1400, backward=True,
+                                 device=DEV)
+    s = synth.default_scale(d)
+    O, L = fa.fa_fwd(q, k, v, s)
+    ref = fa.fa_bwd(q, k, v, O, L, dO, s)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    torch.cuda.synchronize()
+    used0 = torch.cuda.memory_allocated()
+    st = c_noalloc(q, k, v, O, L, dO, dq, dk, dv, s, torch.cuda.current_stream(DEV).cuda_stream)
+    torch.cuda.synchronize()
+    assert st == FA_OK, fa.status_str(st)
+    assert torch.cuda.memory_allocated() == used0
+    for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert torch.equal(x, r), name
+    print("  bit-identical to fa_bwd", flush=True)
