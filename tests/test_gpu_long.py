@@ -116,3 +116,40 @@ def test_long_sampled_rows_and_gradient_identities(N):
                 f"|sum dV - sum dO| / ||dV|| {res_v:.3e}")
         assert res_k <= TOL_BF16_GRAD_REL, ("dK", h)
         assert res_v <= TOL_BF16_GRAD_REL, ("dV", h)
+
+
+def test_heads_beyond_4gib_offsets():
+    """B=2, H=136, N=65536, d=128: each tensor is 4.6 GB, so the last head's
+    rows start 4.55 GB past the base pointer (64-bit per-head offsets in
+    every kernel).  O, LSE and dQ of the first and the last head on 64
+    sampled rows against the oracle, and the dK/dV identities on both."""
+    B, H, N, d = 2, 136, 65536, 128
+    print(f"case heads past 4 GiB: B={B} H={H} N={N} d={d}", flush=True)
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=1500, backward=True,
+                                 device=DEV)
+    s = synth.default_scale(d)
+    O, L = fa.fa_fwd(q, k, v, s)
+    dq, dk, dv = fa.fa_bwd(q, k, v, O, L, dO, s)
+    torch.cuda.synchronize()
+    assert (B * H - 1) * N * d * 2 > (1 << 32)
+    rows = synth.draw_rows(N, 2, 64, seed=1500)
+    for idx, (b, h) in enumerate(((0, 0), (B - 1, H - 1))):
+        r = rows[idx]
+        ridx = torch.from_numpy(r).to(DEV)
+        qh, kh, vh, gh = (f64(x[b, h].cpu()) for x in (q, k, v, dO))
+        Oref, Lref = oracle.sdpa_rows(qh[r], kh, vh, s)
+        dQref, _ = oracle.sdpa_backward_rows(qh[r], kh, vh, gh[r], s)
+        o = f64(O[b, h].index_select(0, ridx).cpu())
+        l = f64(L[b, h].index_select(0, ridx).cpu())
+        g = f64(dq[b, h].index_select(0, ridx).cpu())
+        ma, mn, ml = max_abs(o, Oref), mean_abs(o, Oref), max_abs(l, Lref)
+        rel_o, rel_dq = rel_frobenius(o, Oref), rel_frobenius(g, dQref)
+        say(f"  head ({b},{h}): O max-abs {ma:.3e} mean-abs {mn:.3e} rel {rel_o:.3e}; "
+            f"LSE max-abs {ml:.3e}; dQ rel-Frobenius {rel_dq:.3e}")
+        assert ma <= TOL_BF16_O_MAX and mn <= TOL_BF16_O_MEAN and ml <= TOL_BF16_LSE_MAX
+        assert rel_o <= 2e-2 and rel_dq <= TOL_BF16_GRAD_REL
+        dk64, dv64, g64 = dk[b, h].double(), dv[b, h].double(), dO[b, h].double()
+        res_k = float(dk64.sum(0).norm() / dk64.norm())
+        res_v = float((dv64.sum(0) - g64.sum(0)).norm() / dv64.norm())
+        say(f"  head ({b},{h}): |sum dK| / ||dK|| {res_k:.3e}; |sum dV - sum dO| / ||dV|| {res_v:.3e}")
+        assert res_k <= TOL_BF16_GRAD_REL and res_v <= TOL_BF16_GRAD_REL
