@@ -153,3 +153,37 @@ def test_heads_beyond_4gib_offsets():
         res_v = float((dv64.sum(0) - g64.sum(0)).norm() / dv64.norm())
         say(f"  head ({b},{h}): |sum dK| / ||dK|| {res_k:.3e}; |sum dV - sum dO| / ||dV|| {res_v:.3e}")
         assert res_k <= TOL_BF16_GRAD_REL and res_v <= TOL_BF16_GRAD_REL
+
+
+def test_d64_long_sequence_sampled_rows():
+    """The d = 64 kernels at N = 65536 (B=1, H=4, ragged by 37 keys): O, LSE
+    and dQ on 128 sampled rows per head against the oracle, and the dK/dV
+    identities per head."""
+    B, H, N, d = 1, 4, 65536 - 37, 64
+    print(f"case d=64 long sequence B={B} H={H} N={N}", flush=True)
+    q, k, v, dO = synth.make_qkv(B, H, N, d, torch.bfloat16, seed=1600, backward=True,
+                                 device=DEV)
+    s = synth.default_scale(d)
+    O, L = fa.fa_fwd(q, k, v, s)
+    dq, dk, dv = fa.fa_bwd(q, k, v, O, L, dO, s)
+    torch.cuda.synchronize()
+    rows = synth.draw_rows(N, H, 128, seed=1600)
+    for h in range(H):
+        r = rows[h]
+        ridx = torch.from_numpy(r).to(DEV)
+        qh, kh, vh, gh = (f64(x[0, h].cpu()) for x in (q, k, v, dO))
+        Oref, Lref = oracle.sdpa_rows(qh[r], kh, vh, s)
+        dQref, _ = oracle.sdpa_backward_rows(qh[r], kh, vh, gh[r], s)
+        o = f64(O[0, h].index_select(0, ridx).cpu())
+        l = f64(L[0, h].index_select(0, ridx).cpu())
+        g = f64(dq[0, h].index_select(0, ridx).cpu())
+        ma, mn, ml = max_abs(o, Oref), mean_abs(o, Oref), max_abs(l, Lref)
+        rel_o, rel_dq = rel_frobenius(o, Oref), rel_frobenius(g, dQref)
+        dk64, dv64, g64 = dk[0, h].double(), dv[0, h].double(), dO[0, h].double()
+        res_k = float(dk64.sum(0).norm() / dk64.norm())
+        res_v = float((dv64.sum(0) - g64.sum(0)).norm() / dv64.norm())
+        say(f"  head {h}: O max-abs {ma:.3e} rel {rel_o:.3e}; LSE max-abs {ml:.3e}; "
+            f"dQ rel {rel_dq:.3e}; dK sum {res_k:.3e}; dV sum {res_v:.3e}")
+        assert ma <= TOL_BF16_O_MAX and mn <= TOL_BF16_O_MEAN and ml <= TOL_BF16_LSE_MAX
+        assert rel_o <= 2e-2 and rel_dq <= TOL_BF16_GRAD_REL
+        assert res_k <= TOL_BF16_GRAD_REL and res_v <= TOL_BF16_GRAD_REL
