@@ -6,6 +6,7 @@ fp64 oracle; the calls allocate no device memory; a problem larger than the
 array is refused before anything is enqueued."""
 
 import ctypes
+import gc
 
 import numpy as np
 import pytest
@@ -54,6 +55,7 @@ def test_noalloc_matches_fa_bwd_on_two_calls_second_smaller():
         O, L = fa.fa_fwd(qg, kg, vg, s)
         ref = fa.fa_bwd(qg, kg, vg, O, L, gg, s)
         dq, dk, dv = (torch.full_like(qg, float("nan")) for _ in range(3))
+        gc.collect()   # tensors left by earlier tests are freed now, not during the call
         torch.cuda.synchronize()
         used0 = torch.cuda.memory_allocated()
         free0 = torch.cuda.mem_get_info()[0]
@@ -61,8 +63,8 @@ def test_noalloc_matches_fa_bwd_on_two_calls_second_smaller():
         torch.cuda.synchronize()
         free1 = torch.cuda.mem_get_info()[0]
         assert st == FA_OK, fa.status_str(st)
-        assert torch.cuda.memory_allocated() == used0
-        assert free0 - free1 <= 2 * 1024 * 1024
+        assert torch.cuda.memory_allocated() <= used0   # nothing allocated through torch
+        assert free0 - free1 <= 2 * 1024 * 1024         # nor any device memory at all
         for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             assert torch.equal(x, r), name
         rq, rk, rv, _ = oracle.sdpa_backward(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v),
@@ -95,12 +97,15 @@ def test_noalloc_at_its_maximum_rows():
     O, L = fa.fa_fwd(q, k, v, s)
     ref = fa.fa_bwd(q, k, v, O, L, dO, s)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    gc.collect()
     torch.cuda.synchronize()
     used0 = torch.cuda.memory_allocated()
+    free0 = torch.cuda.mem_get_info()[0]
     st = c_noalloc(q, k, v, O, L, dO, dq, dk, dv, s, torch.cuda.current_stream(DEV).cuda_stream)
     torch.cuda.synchronize()
     assert st == FA_OK, fa.status_str(st)
-    assert torch.cuda.memory_allocated() == used0
+    assert torch.cuda.memory_allocated() <= used0
+    assert free0 - torch.cuda.mem_get_info()[0] <= 2 * 1024 * 1024
     for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         assert torch.equal(x, r), name
     print("  bit-identical to fa_bwd", flush=True)
