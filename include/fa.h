@@ -25,8 +25,17 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     asynchronously; nothing synchronises with the host.
  *   - Arguments are checked before anything is enqueued.  A return other than
- *     FA_OK means nothing was enqueued.  Faults during execution surface at
- *     the caller's next synchronisation.  A launch failure is FA_ERR_HIP.
+ *     FA_OK or FA_ERR_HIP means nothing was enqueued.  A launch failure is
+ *     FA_ERR_HIP; launches of the same call made before it stay enqueued and
+ *     the outputs are then unspecified.  Faults during execution surface at
+ *     the caller's next synchronisation.
+ *   - Sizes set no grid limit of their own: a kernel whose grid would exceed
+ *     2^31 work-items is launched in several chunks of whole heads (or of
+ *     whole blocks of rows), since a single dispatch of 2^32 work-items or
+ *     more is cut short by the runtime without an error.  Only a grid of one
+ *     head that alone exceeds 2^31 work-items is refused, FA_ERR_SHAPE: the
+ *     fp32 calls on key blocks of 8 with N > 2^28, and fa_fwd_split with
+ *     n_split * ceil(N/256) > 2^22.
  *   - B, H or N equal to 0 is an empty problem: FA_OK, nothing enqueued, and
  *     pointers may be NULL.  Negative sizes are FA_ERR_SHAPE.
  *   - `scale` must be finite and > 0 (FA_ERR_SCALE); 1/sqrt(d) rounded to

@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "../../include/fa.h"
+#include "launch_chunks.h"
 #include "validate.h"
 
 // Scratch of fa_bwd_noalloc: D = rowsum(dO * O), one fp32 per query row, for
@@ -45,7 +46,12 @@ namespace {
 using fa::Shape;
 using fa::Span;
 
-inline fa_status from_hip(int e) { return e == 0 ? FA_OK : FA_ERR_HIP; }
+// Launcher status: 0, a hipError_t, or kErrGridTooLarge (one head's grid
+// exceeds a launch; reported before anything is enqueued).
+inline fa_status from_hip(int e) {
+  if (e == 0) return FA_OK;
+  return e == fa::kErrGridTooLarge ? FA_ERR_SHAPE : FA_ERR_HIP;
+}
 inline hipStream_t as_stream(fa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 struct Sizes {

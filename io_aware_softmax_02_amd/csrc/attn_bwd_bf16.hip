@@ -23,6 +23,7 @@
 // buffer->LDS loads (reads past the end of a head return 0, which is what a
 // ragged last tile needs): dQ double-buffers its K/V tiles with one barrier
 // per tile; dK/dV triple-buffers its Q/dO tiles (below).
+#include "launch_chunks.h"
 #include "lds_tile.h"
 
 namespace fa {
@@ -642,9 +643,13 @@ template <int D>
 int launch_pre(const uint16_t* o, const uint16_t* dO, float* delta, int64_t rows,
                hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, o, dO, delta, rows);
-  return (int)hipGetLastError();
+  // Chunks of whole blocks of RPB rows.
+  return launch_in_chunks((rows + RPB - 1) / RPB, 256, [&](int64_t b0, int64_t nb) {
+    const int64_t r0 = b0 * RPB, nr = std::min(nb * RPB, rows - r0);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)nb), dim3(256), 0, stream, o + r0 * D,
+                       dO + r0 * D, delta + r0, nr);
+    return (int)hipGetLastError();
+  });
 }
 
 template <int D>
@@ -652,13 +657,18 @@ int launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const f
                 const uint16_t* dO, const float* delta, uint16_t* dk, uint16_t* dv, int64_t BH,
                 int64_t N, float scale, hipStream_t stream) {
   using C = DkdvCfg<D>;
+  const int nkt = (int)((N + C::BK - 1) / C::BK);
+  const int64_t per_head = (int64_t)nkt * C::THREADS;
+  if (!unit_fits(per_head)) return kErrGridTooLarge;
   hipError_t e = allow_lds(bwd_dkdv_kernel<D>, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
-  const int nkt = (int)((N + C::BK - 1) / C::BK);
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(nkt * BH)), dim3(C::THREADS),
-                     C::LDS_BYTES, stream, q, k, v, lse, dO, delta, dk, dv, (int)N, nkt,
-                     scale * kLog2e, scale);
-  return (int)hipGetLastError();
+  return launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D, roff = h0 * N;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(nkt * nh)), dim3(C::THREADS),
+                       C::LDS_BYTES, stream, q + off, k + off, v + off, lse + roff, dO + off,
+                       delta + roff, dk + off, dv + off, (int)N, nkt, scale * kLog2e, scale);
+    return (int)hipGetLastError();
+  });
 }
 
 template <int D, int RA = kReadAhead, int SA = kStepAhead>
@@ -666,13 +676,19 @@ int launch_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const flo
                 const uint16_t* dO, const float* delta, uint16_t* dq, int64_t BH, int64_t N,
                 float scale, hipStream_t stream) {
   using C = DqCfg<D>;
+  const int nqt = (int)((N + C::BQ - 1) / C::BQ);
+  const int64_t per_head = (int64_t)nqt * C::THREADS;
+  if (!unit_fits(per_head)) return kErrGridTooLarge;
   hipError_t e = allow_lds(bwd_dq_kernel<D, RA, SA>, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
-  const int nqt = (int)((N + C::BQ - 1) / C::BQ);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, RA, SA>), dim3((unsigned)(nqt * BH)), dim3(C::THREADS),
-                     C::LDS_BYTES, stream, q, k, v, lse, dO, delta, dq, (int)N, nqt,
-                     scale * kLog2e, scale);
-  return (int)hipGetLastError();
+  return launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D, roff = h0 * N;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, RA, SA>), dim3((unsigned)(nqt * nh)),
+                       dim3(C::THREADS), C::LDS_BYTES, stream, q + off, k + off, v + off,
+                       lse + roff, dO + off, delta + roff, dq + off, (int)N, nqt,
+                       scale * kLog2e, scale);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace

@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "launch_chunks.h"
+
 namespace fa {
 namespace {
 
@@ -259,31 +261,49 @@ int launch_fwd_f32(const float* q, const float* k, const float* v, float* o, flo
                    int64_t BH, int64_t N, int64_t d, float scale, hipStream_t stream) {
   if (f32_key_block(N, d) != T)
     return launch_fwd_f32_mfma(q, k, v, o, lse, BH, N, d, scale, stream);
-  const int ntq = (int)((N + T - 1) / T);
-  hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)(ntq * BH)), dim3(64), 0, stream, q, k, v,
-                     o, lse, (int)N, (int)d, ntq, scale);
-  return (int)hipGetLastError();
+  const int64_t ntq = (N + T - 1) / T;
+  return launch_in_chunks(BH, ntq * 64, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * d;
+    hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)(ntq * nh)), dim3(64), 0, stream, q + off,
+                       k + off, v + off, o + off, lse + h0 * N, (int)N, (int)d, (int)ntq, scale);
+    return (int)hipGetLastError();
+  });
 }
 
 int launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                    const float* lse, const float* dO, float* dq, float* dk, float* dv,
                    float* delta, int64_t BH, int64_t N, int64_t d, float scale,
                    hipStream_t stream) {
+  const bool small = f32_key_block(N, d) == T;
+  const int64_t nt = (N + T - 1) / T;
+  // The 8-row kernels' grid of one head must fit one launch (checked before
+  // the preprocess is enqueued; the matrix-core kernels check their own).
+  if (small && !unit_fits(nt * 64)) return kErrGridTooLarge;
   const int64_t rows = BH * N;
-  hipLaunchKernelGGL(bwd_pre_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                     stream, o, dO, delta, rows, (int)d);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  if (f32_key_block(N, d) != T)
+  int e = launch_in_chunks((rows + 255) / 256, 256, [&](int64_t b0, int64_t nb) {
+    const int64_t r0 = b0 * 256, nr = std::min(nb * 256, rows - r0);
+    hipLaunchKernelGGL(bwd_pre_f32_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
+                       o + r0 * d, dO + r0 * d, delta + r0, nr, (int)d);
+    return (int)hipGetLastError();
+  });
+  if (e != 0) return e;
+  if (!small)
     return launch_bwd_f32_mfma(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, d, scale, stream);
-  const int nt = (int)((N + T - 1) / T);
-  hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k,
-                     v, lse, dO, delta, dk, dv, (int)N, (int)d, nt, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)(nt * BH)), dim3(64), 0, stream, q, k, v,
-                     lse, dO, delta, dq, (int)N, (int)d, nt, scale);
-  return (int)hipGetLastError();
+  e = launch_in_chunks(BH, nt * 64, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * d, roff = h0 * N;
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nt * nh)), dim3(64), 0, stream,
+                       q + off, k + off, v + off, lse + roff, dO + off, delta + roff, dk + off,
+                       dv + off, (int)N, (int)d, (int)nt, scale);
+    return (int)hipGetLastError();
+  });
+  if (e != 0) return e;
+  return launch_in_chunks(BH, nt * 64, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * d, roff = h0 * N;
+    hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)(nt * nh)), dim3(64), 0, stream,
+                       q + off, k + off, v + off, lse + roff, dO + off, delta + roff, dq + off,
+                       (int)N, (int)d, (int)nt, scale);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace fa

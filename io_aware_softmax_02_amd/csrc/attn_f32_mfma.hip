@@ -23,6 +23,7 @@
 // registers one tile ahead (zero past N) and double-buffered; one barrier per
 // tile.
 #include "device_common.h"
+#include "launch_chunks.h"
 
 namespace fa {
 namespace {
@@ -192,13 +193,19 @@ int launch_fwd(const float* q, const float* k, const float* v, float* o, float* 
                int64_t N, float scale, hipStream_t stream) {
   using C = F32Cfg<D>;
   const int ntq = (int)((N + C::BR - 1) / C::BR);
+  const int64_t per_head = (int64_t)ntq * C::THREADS;
+  if (!unit_fits(per_head)) return kErrGridTooLarge;
   auto kern = fwd_f32_mfma_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(ntq * BH)), dim3(C::THREADS), C::LDS_BYTES, stream,
-                     q, k, v, o, lse, (int)N, ntq, scale * kLog2e);
-  return (int)hipGetLastError();
+  return launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ntq * nh)), dim3(C::THREADS), C::LDS_BYTES, stream,
+                       q + off, k + off, v + off, o + off, lse + h0 * N, (int)N, ntq,
+                       scale * kLog2e);
+    return (int)hipGetLastError();
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -493,6 +500,8 @@ int launch_bwd(const float* q, const float* k, const float* v, const float* lse,
                int64_t N, float scale, hipStream_t stream) {
   using C = F32BwdCfg<D>;
   const int nt = (int)((N + C::BRES - 1) / C::BRES);
+  const int64_t per_head = (int64_t)nt * C::THREADS;
+  if (!unit_fits(per_head)) return kErrGridTooLarge;
   auto kd = bwd_dkdv_f32_mfma_kernel<D>;
   auto kq = bwd_dq_f32_mfma_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void*)kd,
@@ -501,13 +510,21 @@ int launch_bwd(const float* q, const float* k, const float* v, const float* lse,
   e = hipFuncSetAttribute((const void*)kq, hipFuncAttributeMaxDynamicSharedMemorySize,
                           C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(kd, dim3((unsigned)(nt * BH)), dim3(C::THREADS), C::LDS_BYTES, stream, q,
-                     k, v, lse, dO, delta, dk, dv, (int)N, nt, scale * kLog2e, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(kq, dim3((unsigned)(nt * BH)), dim3(C::THREADS), C::LDS_BYTES, stream, q,
-                     k, v, lse, dO, delta, dq, (int)N, nt, scale * kLog2e, scale);
-  return (int)hipGetLastError();
+  const int r = launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D, roff = h0 * N;
+    hipLaunchKernelGGL(kd, dim3((unsigned)(nt * nh)), dim3(C::THREADS), C::LDS_BYTES, stream,
+                       q + off, k + off, v + off, lse + roff, dO + off, delta + roff, dk + off,
+                       dv + off, (int)N, nt, scale * kLog2e, scale);
+    return (int)hipGetLastError();
+  });
+  if (r != 0) return r;
+  return launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D, roff = h0 * N;
+    hipLaunchKernelGGL(kq, dim3((unsigned)(nt * nh)), dim3(C::THREADS), C::LDS_BYTES, stream,
+                       q + off, k + off, v + off, lse + roff, dO + off, delta + roff, dq + off,
+                       (int)N, nt, scale * kLog2e, scale);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace

@@ -43,6 +43,7 @@
 // and each workgroup handles one range of one query tile, writing that
 // range's own normalised output (fp32) and LSE.  The ranges are recombined
 // by the merge kernel (attn_merge.hip) with the same rescale identity.
+#include "launch_chunks.h"
 #include "lds_tile.h"
 
 namespace fa {
@@ -332,14 +333,22 @@ int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, flo
              int64_t BH, int64_t N, float scale, int nsplit, hipStream_t stream) {
   using C = FwdCfg<D, BC, NWAVES>;
   const int ntq = (int)((N + C::BR - 1) / C::BR);
-  const int64_t nwg = (int64_t)ntq * BH * nsplit;
+  const int64_t per_head = (int64_t)ntq * nsplit * C::THREADS;
+  if (!unit_fits(per_head)) return kErrGridTooLarge;
   auto kern = fwd_bf16_kernel<D, BC, MINW, PRIO, NWAVES, SPLIT, RA, SA>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(C::THREADS), C::LDS_BYTES, stream, q, k,
-                     v, o, lse, (int)N, ntq, scale * kLog2e, nsplit, BH * N);
-  return (int)hipGetLastError();
+  // Chunks of whole heads; the partials keep their stride of B*H*N rows.
+  return launch_in_chunks(BH, per_head, [&](int64_t h0, int64_t nh) {
+    const int64_t off = h0 * N * D;
+    void* oc = SPLIT ? (void*)(static_cast<float*>(o) + off)
+                     : (void*)(static_cast<uint16_t*>(o) + off);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ntq * nh * nsplit)), dim3(C::THREADS),
+                       C::LDS_BYTES, stream, q + off, k + off, v + off, oc, lse + h0 * N, (int)N,
+                       ntq, scale * kLog2e, nsplit, BH * N);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace

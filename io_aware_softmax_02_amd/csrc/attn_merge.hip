@@ -15,14 +15,17 @@
 // (no key) contributes nothing, whatever its O_p holds; a row with no range
 // holding a key gets O = 0 and LSE = -inf.
 #include "device_common.h"
+#include "launch_chunks.h"
 
 namespace fa {
 namespace {
 
+// `rows` rows of this launch, each part `part_stride` rows apart.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part,
                                                     int nsplit, int64_t rows,
+                                                    int64_t part_stride,
                                                     uint16_t* __restrict__ o,
                                                     float* __restrict__ lse) {
   constexpr int LPR = D / 4;          // lanes per row
@@ -44,9 +47,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int p = p0 + c;
-      lp[c] = p < nsplit ? lse_part[p * rows + row] : -INFINITY;
-      op[c] = p < nsplit ? *reinterpret_cast<const f32x4*>(o_part + (p * rows + row) * D + col)
-                         : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      lp[c] = p < nsplit ? lse_part[p * part_stride + row] : -INFINITY;
+      op[c] = p < nsplit
+                  ? *reinterpret_cast<const f32x4*>(o_part + (p * part_stride + row) * D + col)
+                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     float mc = m;
 #pragma unroll
@@ -84,9 +88,13 @@ template <int D>
 int launch_merge(const float* o_part, const float* lse_part, int nsplit, int64_t rows,
                  uint16_t* o, float* lse, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 4);
-  hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, o_part, lse_part, nsplit, rows, o, lse);
-  return (int)hipGetLastError();
+  // Chunks of whole blocks of RPB rows; each part keeps its stride of `rows`.
+  return launch_in_chunks((rows + RPB - 1) / RPB, 256, [&](int64_t b0, int64_t nb) {
+    const int64_t r0 = b0 * RPB, nr = std::min(nb * RPB, rows - r0);
+    hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)nb), dim3(256), 0, stream,
+                       o_part + r0 * D, lse_part + r0, nsplit, nr, rows, o + r0 * D, lse + r0);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace

@@ -20,8 +20,9 @@ struct Shape {
   int64_t rows() const { return B * H * N; }
 };
 
-// Largest tensor accepted: 2^40 elements keeps every byte offset, grid
-// dimension and per-head offset far inside int64 and the launch limits.
+// Largest tensor accepted: 2^40 elements keeps every byte offset and
+// per-head offset far inside int64.  Grids are cut into launches of at most
+// 2^31 work-items by the launchers, so the total size sets no grid limit.
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 inline fa_status check_shape(const Shape& s, bool bf16) {
@@ -43,8 +44,6 @@ inline fa_status check_shape(const Shape& s, bool bf16) {
   const int64_t bh = s.B * s.H;
   if (s.N > lim / bh) return FA_ERR_SHAPE;
   if (s.d > lim / (bh * s.N)) return FA_ERR_SHAPE;
-  // Grid sizes: one workgroup per (row tile, head) in a 1-D grid.
-  if (bh * ((s.N + 7) / 8) > (int64_t(1) << 31) - 1) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -106,12 +105,11 @@ inline int64_t split_max(const Shape& s, int64_t tile) {
 }
 
 // n_split partial tensors of the shape: the count must be >= 1 and the
-// partials must stay inside the size limits (and the grid inside int32).
+// partials must stay inside the size limit.
 inline fa_status check_parts(const Shape& s, int64_t n_split) {
   if (n_split < 1) return FA_ERR_SHAPE;
   if (s.empty()) return FA_OK;
   if (n_split > kMaxElems / s.elems()) return FA_ERR_SHAPE;
-  if (s.B * s.H * ((s.N + 7) / 8) > ((int64_t(1) << 31) - 1) / n_split) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

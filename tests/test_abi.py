@@ -140,6 +140,29 @@ def test_split_and_merge_argument_checks(lib):
     assert lib.fa_merge(0, 0, 3, 0, 0, 0, 4, 64, 128, None) == L.FA_OK
 
 
+# Fake addresses 1 TiB apart, for shapes whose tensors are large.
+FAR = [(i + 1) << 40 for i in range(12)]
+
+
+def test_single_head_grid_beyond_one_launch_is_refused(lib):
+    """Grids are launched in chunks of whole heads of at most 2^31
+    work-items; a head whose own grid exceeds that is FA_ERR_SHAPE, returned
+    before any HIP call (the argument checks all pass for these shapes)."""
+    from io_aware_softmax_02_amd import _lib as L
+    # fp32 on key blocks of 8: 64 lanes per 8 query rows, ceil(N/8) * 64 > 2^31
+    N = (1 << 28) + 1
+    assert lib.fa_f32_key_block(N, 17) == 8
+    assert fwd(lib, ptrs=FAR[:5], N=N, d=17, f32=True) == L.FA_ERR_SHAPE
+    ws = lib.fa_bwd_f32_workspace_bytes(1, 1, N, 17)
+    assert bwd(lib, ptrs=FAR[:9], ws=FAR[9], ws_bytes=ws, N=N, d=17, f32=True) == L.FA_ERR_SHAPE
+    # split forward: 512 lanes per 256 query rows per key range; at N = 2^23
+    # that is 2^15 * n_split * 512 lanes, beyond 2^31 from n_split = 129 on
+    q, k, v, op, lp = FAR[:5]
+    assert lib.fa_fwd_split_max(1, 1, 1 << 23, 64) == 1 << 17
+    assert lib.fa_fwd_split(q, k, v, op, lp, 1, 1, 1 << 23, 64, 0.125, 129, None) == \
+        L.FA_ERR_SHAPE
+
+
 def test_empty_problems_are_noops(lib):
     from io_aware_softmax_02_amd import _lib as L
     for B, H, N in ((0, 1, 64), (1, 0, 64), (1, 1, 0)):
