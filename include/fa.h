@@ -22,8 +22,11 @@
  *     are reentrant.
  *   - Outputs are fully overwritten (never accumulated into) and must not
  *     overlap any input or each other (FA_ERR_ALIAS).
- *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
- *     asynchronously; nothing synchronises with the host.
+ *   - `stream` is a hipStream_t (NULL = the null stream of the current
+ *     device).  Work is enqueued asynchronously; nothing synchronises with
+ *     the host.  The kernels run on the stream's device, which the call
+ *     makes current while it launches and then restores the caller's; the
+ *     tensors must be on that device.
  *   - Arguments are checked before anything is enqueued.  A return other than
  *     FA_OK or FA_ERR_HIP means nothing was enqueued.  A launch failure is
  *     FA_ERR_HIP; launches of the same call made before it stay enqueued and

@@ -12,6 +12,7 @@ Tensors are contiguous [B, H, N, d] on a GPU; ``lse`` is [B, H, N] float32.
 
 from __future__ import annotations
 
+import contextlib
 import math
 from typing import Optional, Tuple
 
@@ -51,16 +52,27 @@ def _shape4(x: torch.Tensor, name: str, dtype: torch.dtype):
     return tuple(x.shape)
 
 
-def _same(shape, x: torch.Tensor, name: str, dtype: torch.dtype):
+def _same(shape, x: torch.Tensor, name: str, dtype: torch.dtype, dev: torch.device):
     if _shape4(x, name, dtype) != shape:
         raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
+    if x.device != dev:
+        raise ValueError(f"{name} is on {x.device}, the other tensors on {dev}")
 
 
-def _rows(x: torch.Tensor, name: str, shape) -> None:
+def _rows(x: torch.Tensor, name: str, shape, dev: torch.device) -> None:
     B, H, N, _ = shape
-    if x.device.type != "cuda" or x.dtype != torch.float32 or tuple(x.shape) != (B, H, N) \
-            or not x.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 [B, H, N] GPU tensor")
+    if not isinstance(x, torch.Tensor) or x.device != dev or x.dtype != torch.float32 \
+            or tuple(x.shape) != (B, H, N) or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 [B, H, N] tensor on {dev}")
+
+
+def _on(dev: torch.device):
+    """Device context of a call.  The default stream's handle (0) means the
+    null stream of the current device, so a call on another device's tensors
+    makes that device current for the call."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
 
 
 def _stream(dev: torch.device, stream) -> int:
@@ -75,20 +87,21 @@ def _ptr(x: Optional[torch.Tensor]) -> int:
 
 def _fwd(fn, where, dtype, q, k, v, scale, o, lse, stream):
     shape = _shape4(q, "q", dtype)
-    _same(shape, k, "k", dtype)
-    _same(shape, v, "v", dtype)
+    dev = q.device
+    _same(shape, k, "k", dtype, dev)
+    _same(shape, v, "v", dtype, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
     if o is None:
         o = torch.empty_like(q)
     else:
-        _same(shape, o, "o", dtype)
+        _same(shape, o, "o", dtype, dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
-        _rows(lse, "lse", shape)
-    with torch.cuda.device(q.device):
+        _rows(lse, "lse", shape, dev)
+    with _on(dev):
         _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                   _stream(q.device, stream)), where)
     return o, lse
@@ -110,8 +123,9 @@ def fa_fwd_split(q, k, v, n_split: int, scale: Optional[float] = None, o_part=No
     """Split-KV forward.  Returns (o_part fp32 [n_split,B,H,N,d], lse_part fp32
     [n_split,B,H,N]): each key range's own normalised output and LSE."""
     shape = _shape4(q, "q", torch.bfloat16)
-    _same(shape, k, "k", torch.bfloat16)
-    _same(shape, v, "v", torch.bfloat16)
+    dev = q.device
+    _same(shape, k, "k", torch.bfloat16, dev)
+    _same(shape, v, "v", torch.bfloat16, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
@@ -120,8 +134,8 @@ def fa_fwd_split(q, k, v, n_split: int, scale: Optional[float] = None, o_part=No
         o_part = torch.empty((max(n, 0), B, H, N, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((max(n, 0), B, H, N), dtype=torch.float32, device=q.device)
-    _parts(o_part, lse_part, n, shape)
-    with torch.cuda.device(q.device):
+    _parts(o_part, lse_part, n, shape, dev)
+    with _on(dev):
         _check(LIB.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part),
                                 B, H, N, d, float(scale), n, _stream(q.device, stream)),
                "fa_fwd_split")
@@ -136,26 +150,29 @@ def fa_merge(o_part, lse_part, o=None, lse=None, stream=None
         raise ValueError("o_part must be a [P, B, H, N, d] tensor")
     n = int(o_part.shape[0])
     shape = tuple(o_part.shape[1:])
-    _parts(o_part, lse_part, n, shape)
+    dev = o_part.device
+    _parts(o_part, lse_part, n, shape, dev)
     B, H, N, d = shape
     if o is None:
         o = torch.empty(shape, dtype=torch.bfloat16, device=o_part.device)
     else:
-        _same(shape, o, "o", torch.bfloat16)
+        _same(shape, o, "o", torch.bfloat16, dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
     else:
-        _rows(lse, "lse", shape)
-    with torch.cuda.device(o_part.device):
+        _rows(lse, "lse", shape, dev)
+    with _on(dev):
         _check(LIB.fa_merge(_ptr(o_part), _ptr(lse_part), n, _ptr(o), _ptr(lse), B, H, N, d,
                             _stream(o_part.device, stream)), "fa_merge")
     return o, lse
 
 
-def _parts(o_part, lse_part, n: int, shape) -> None:
+def _parts(o_part, lse_part, n: int, shape, dev: torch.device) -> None:
     for x, name, tail in ((o_part, "o_part", tuple(shape)), (lse_part, "lse_part", tuple(shape[:3]))):
         if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
             raise ValueError(f"{name} must be a GPU tensor")
+        if x.device != dev:
+            raise ValueError(f"{name} is on {x.device}, the other tensors on {dev}")
         if x.dtype != torch.float32 or not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous float32")
         if tuple(x.shape) != (max(n, 0),) + tail:
@@ -185,9 +202,10 @@ def fa_bwd_f32_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def _bwd(fn, wsfn, where, dtype, q, k, v, o, lse, dO, scale, dq, dk, dv, workspace, stream):
     shape = _shape4(q, "q", dtype)
+    dev = q.device
     for x, name in ((k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
-        _same(shape, x, name, dtype)
-    _rows(lse, "lse", shape)
+        _same(shape, x, name, dtype, dev)
+    _rows(lse, "lse", shape, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
@@ -196,14 +214,17 @@ def _bwd(fn, wsfn, where, dtype, q, k, v, o, lse, dO, scale, dq, dk, dv, workspa
         if x is None:
             x = torch.empty_like(q)
         else:
-            _same(shape, x, name, dtype)
+            _same(shape, x, name, dtype, dev)
         outs.append(x)
     dq, dk, dv = outs
     need = int(wsfn(B, H, N, d))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device != dev \
+            or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
     ws_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
+    with _on(dev):
         _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
                   _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, float(scale),
                   _stream(q.device, stream)), where)
@@ -224,9 +245,10 @@ def fa_bwd_noalloc(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, 
     dq, dk, dv to make this call allocate nothing either.  Calls that overlap
     in time on one GPU race.  Returns (dq, dk, dv)."""
     shape = _shape4(q, "q", torch.bfloat16)
+    dev = q.device
     for x, name in ((k, "k"), (v, "v"), (o, "o"), (dO, "dO")):
-        _same(shape, x, name, torch.bfloat16)
-    _rows(lse, "lse", shape)
+        _same(shape, x, name, torch.bfloat16, dev)
+    _rows(lse, "lse", shape, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
@@ -235,10 +257,10 @@ def fa_bwd_noalloc(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, 
         if x is None:
             x = torch.empty_like(q)
         else:
-            _same(shape, x, name, torch.bfloat16)
+            _same(shape, x, name, torch.bfloat16, dev)
         outs.append(x)
     dq, dk, dv = outs
-    with torch.cuda.device(q.device):
+    with _on(dev):
         _check(LIB.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                                   _stream(q.device, stream)), "fa_bwd_noalloc")
@@ -255,13 +277,14 @@ def fa_bwd_f32(q, k, v, o, lse, dO, scale: Optional[float] = None, dq=None, dk=N
 def fa_bwd_preprocess(o, dO, delta=None, stream=None):
     """Stage 1 of fa_bwd: delta = rowsum(dO * o), fp32 [B,H,N]."""
     shape = _shape4(o, "o", torch.bfloat16)
-    _same(shape, dO, "dO", torch.bfloat16)
+    dev = o.device
+    _same(shape, dO, "dO", torch.bfloat16, dev)
     B, H, N, d = shape
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
     else:
-        _rows(delta, "delta", shape)
-    with torch.cuda.device(o.device):
+        _rows(delta, "delta", shape, dev)
+    with _on(dev):
         _check(LIB.fa_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(delta), B, H, N, d,
                                      _stream(o.device, stream)), "fa_bwd_preprocess")
     return delta
@@ -271,18 +294,19 @@ def fa_bwd_dkdv(q, k, v, lse, dO, delta, scale: Optional[float] = None, dk=None,
                 stream=None):
     """Stage 2 of fa_bwd.  Returns (dk, dv)."""
     shape = _shape4(q, "q", torch.bfloat16)
+    dev = q.device
     for x, name in ((k, "k"), (v, "v"), (dO, "dO")):
-        _same(shape, x, name, torch.bfloat16)
-    _rows(lse, "lse", shape)
-    _rows(delta, "delta", shape)
+        _same(shape, x, name, torch.bfloat16, dev)
+    _rows(lse, "lse", shape, dev)
+    _rows(delta, "delta", shape, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    _same(shape, dk, "dk", torch.bfloat16)
-    _same(shape, dv, "dv", torch.bfloat16)
-    with torch.cuda.device(q.device):
+    _same(shape, dk, "dk", torch.bfloat16, dev)
+    _same(shape, dv, "dv", torch.bfloat16, dev)
+    with _on(dev):
         _check(LIB.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(delta),
                                _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                                _stream(q.device, stream)), "fa_bwd_dkdv")
@@ -292,16 +316,17 @@ def fa_bwd_dkdv(q, k, v, lse, dO, delta, scale: Optional[float] = None, dk=None,
 def fa_bwd_dq(q, k, v, lse, dO, delta, scale: Optional[float] = None, dq=None, stream=None):
     """Stage 3 of fa_bwd.  Returns dq."""
     shape = _shape4(q, "q", torch.bfloat16)
+    dev = q.device
     for x, name in ((k, "k"), (v, "v"), (dO, "dO")):
-        _same(shape, x, name, torch.bfloat16)
-    _rows(lse, "lse", shape)
-    _rows(delta, "delta", shape)
+        _same(shape, x, name, torch.bfloat16, dev)
+    _rows(lse, "lse", shape, dev)
+    _rows(delta, "delta", shape, dev)
     B, H, N, d = shape
     if scale is None:
         scale = default_scale(d)
     dq = torch.empty_like(q) if dq is None else dq
-    _same(shape, dq, "dq", torch.bfloat16)
-    with torch.cuda.device(q.device):
+    _same(shape, dq, "dq", torch.bfloat16, dev)
+    with _on(dev):
         _check(LIB.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(delta),
                              _ptr(dq), B, H, N, d, float(scale), _stream(q.device, stream)),
                "fa_bwd_dq")

@@ -92,6 +92,38 @@ fa_status check_bwd(const void* q, const void* k, const void* v, const void* o,
                          {{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {ws, wsz}});
 }
 
+// A call's kernels run on its stream's device, while kernel attributes (the
+// dynamic LDS size) are set on the current device.  For a stream of another
+// device, that device is made current for the call and the caller's device
+// is restored afterwards; the null stream is the current device's.  A stream
+// whose device cannot be read is left to the launch to report.
+class OnStreamDevice {
+ public:
+  explicit OnStreamDevice(hipStream_t st) {
+    int dev = -1;
+    if (st == nullptr || hipStreamGetDevice(st, &dev) != hipSuccess) return;
+    if (hipGetDevice(&prev_) != hipSuccess) return;
+    if (dev != prev_) {
+      ok_ = hipSetDevice(dev) == hipSuccess;
+      switched_ = ok_;
+    }
+  }
+  ~OnStreamDevice() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+  OnStreamDevice(const OnStreamDevice&) = delete;
+  OnStreamDevice& operator=(const OnStreamDevice&) = delete;
+  bool ok() const { return ok_; }
+
+ private:
+  int prev_ = -1;
+  bool ok_ = true, switched_ = false;
+};
+
+#define FA_ON_STREAM_DEVICE(st)                   \
+  const OnStreamDevice fa_on_device_(st);         \
+  if (!fa_on_device_.ok()) return FA_ERR_HIP
+
 // Device address of `scratch` on device `dev`, looked up once per device
 // with that device current (each device holds the array at its own address).
 constexpr int kMaxDevices = 64;
@@ -140,6 +172,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   const Shape s{B, H, N, d};
   FA_TRY(check_fwd(q, k, v, o, lse, s, scale, true));
   if (s.empty()) return FA_OK;
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
 }
 
@@ -163,6 +196,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
   const size_t np = static_cast<size_t>(n_split);
   FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}},
                          {{o_part, np * z.tensor * 2}, {lse_part, np * z.rows}}));
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_fwd_split_bf16(q, k, v, o_part, lse_part, B * H, N, d, scale,
                                             static_cast<int>(n_split), as_stream(stream)));
 }
@@ -178,6 +212,7 @@ fa_status fa_merge(const float* o_part, const float* lse_part, int64_t n_split, 
   const size_t np = static_cast<size_t>(n_split);
   FA_TRY(fa::check_alias({{o_part, np * z.tensor * 2}, {lse_part, np * z.rows}},
                          {{o, z.tensor}, {lse, z.rows}}));
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_merge_bf16(o_part, lse_part, static_cast<int>(n_split), s.rows(),
                                         d, o, lse, as_stream(stream)));
 }
@@ -194,6 +229,7 @@ fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta, int64_t
   FA_TRY(fa::check_ptrs({o, dO, delta}, 16));
   const Sizes z = sizes(s, 2);
   FA_TRY(fa::check_alias({{o, z.tensor}, {dO, z.tensor}}, {{delta, z.rows}}));
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, as_stream(stream)));
 }
 
@@ -209,6 +245,7 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* 
   FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {lse, z.rows},
                           {dO, z.tensor}, {delta, z.rows}},
                          {{dk, z.tensor}, {dv, z.tensor}}));
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale,
                                            as_stream(stream)));
 }
@@ -225,6 +262,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
   FA_TRY(fa::check_alias({{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {lse, z.rows},
                           {dO, z.tensor}, {delta, z.rows}},
                          {{dq, z.tensor}}));
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale,
                                          as_stream(stream)));
 }
@@ -238,6 +276,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (s.empty()) return FA_OK;
   float* delta = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
+  FA_ON_STREAM_DEVICE(st);
   FA_TRY(from_hip(fa::launch_bwd_pre_bf16(o, dO, delta, s.rows(), d, st)));
   FA_TRY(from_hip(fa::launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, st)));
   return from_hip(fa::launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, B * H, N, d, scale, st));
@@ -258,12 +297,9 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
                           {lse, z.rows}, {dO, z.tensor}},
                          {{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}}));
   hipStream_t st = as_stream(stream);
-  int dev = -1;
-  if (st == nullptr) {
-    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
-  } else if (hipStreamGetDevice(st, &dev) != hipSuccess) {
-    return FA_ERR_HIP;
-  }
+  FA_ON_STREAM_DEVICE(st);
+  int dev = -1;   // the stream's device, current from here on
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
   float* delta = nullptr;
   FA_TRY(scratch_on(dev, &delta));
   // Rows [0, B*H*N) of the scratch are written by the preprocess kernel
@@ -280,6 +316,7 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
   const Shape s{B, H, N, d};
   FA_TRY(check_fwd(q, k, v, o, lse, s, scale, false));
   if (s.empty()) return FA_OK;
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, as_stream(stream)));
 }
 
@@ -299,6 +336,7 @@ fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float
   const Shape s{B, H, N, d};
   FA_TRY(check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, s, scale, false));
   if (s.empty()) return FA_OK;
+  FA_ON_STREAM_DEVICE(as_stream(stream));
   return from_hip(fa::launch_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv,
                                      static_cast<float*>(workspace), B * H, N, d, scale,
                                      as_stream(stream)));

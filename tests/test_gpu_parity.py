@@ -430,6 +430,27 @@ def test_bf16_backward_is_deterministic_and_stages_match():
     assert (delta.double() - dref).abs().max().item() <= 1e-4
 
 
+def test_binding_rejects_tensors_off_the_device():
+    # Every tensor of a call must sit on the device of its first tensor; a
+    # host-side LSE, workspace or partial is refused before the library runs.
+    say("case binding device checks")
+    q, k, v, dO = (gpu(x) for x in synth.make_qkv(1, 2, 64, 64, torch.bfloat16, 7,
+                                                   backward=True))
+    O, L = fa.fa_fwd(q, k, v)
+    with pytest.raises(ValueError, match="on cuda"):
+        fa.fa_fwd(q, k, v, lse=torch.empty(1, 2, 64))
+    with pytest.raises(ValueError, match="workspace"):
+        fa.fa_bwd(q, k, v, O, L, dO, workspace=torch.empty(1 << 12, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="on cuda"):
+        fa.fa_bwd_dq(q, k, v, L.cpu(), dO, torch.zeros_like(L))
+    op = torch.zeros(2, 1, 2, 64, 64, device=DEV)
+    with pytest.raises(ValueError):
+        fa.fa_merge(op, torch.zeros(2, 1, 2, 64))
+    dq, dk, dv = fa.fa_bwd(q, k, v, O, L, dO)      # still fine with everything on the GPU
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dq.float()).all())
+
+
 def test_side_stream_and_empty_and_errors():
     say("case streams, empty problems, error paths")
     q, k, v = (gpu(x) for x in synth.make_qkv(1, 2, 256, 64, torch.bfloat16, 5)[:3])
