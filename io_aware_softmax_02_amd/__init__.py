@@ -24,7 +24,7 @@ from ._lib import LIB, FAError, FA_OK, FA_BWD_NOALLOC_MAX_ROWS, status_str  # no
 __all__ = [
     "fa_fwd", "fa_fwd_split_max", "fa_fwd_split", "fa_merge", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
     "fa_bwd_dq", "fa_f32_key_block", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_f32_workspace_bytes",
-    "default_scale", "FAError", "status_str",
+    "default_scale", "FAError", "status_str", "forward", "backward",
 ]
 
 
@@ -331,3 +331,10 @@ def fa_bwd_dq(q, k, v, lse, dO, delta, scale: Optional[float] = None, dq=None, s
                              _ptr(dq), B, H, N, d, float(scale), _stream(q.device, stream)),
                "fa_bwd_dq")
     return dq
+
+
+# Short names for the two calls of the hot path: forward(q, k, v, scale=None)
+# -> (o, lse) and backward(q, k, v, o, lse, dO, scale=None) -> (dq, dk, dv),
+# bf16; a non-OK status raises FAError (a RuntimeError).
+forward = fa_fwd
+backward = fa_bwd

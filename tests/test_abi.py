@@ -211,6 +211,12 @@ def test_bwd_argument_checks(lib):
                          float("nan"), None) == L.FA_ERR_SCALE
 
 
+def test_python_short_names():
+    import io_aware_softmax_02_amd as fa
+    assert fa.forward is fa.fa_fwd and fa.backward is fa.fa_bwd
+    assert issubclass(fa.FAError, RuntimeError)
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     import io_aware_softmax_02_amd as fa
