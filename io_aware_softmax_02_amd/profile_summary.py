@@ -45,7 +45,8 @@ KERNELS = {"fwd_bf16_kernel": "fwd_bf16", "bwd_dkdv_kernel": "bwd_dkdv_bf16",
 # Sources whose digest a traffic record carries: a record is only reported
 # while the kernels it measured are unchanged.
 TRAFFIC_SOURCES = ["io_aware_softmax_02_amd/csrc/" + x for x in
-                   ("attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "lds_tile.h", "device_common.h")] + \
+                   ("attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "lds_tile.h", "device_common.h",
+                    "launch_chunks.h")] + \
                   ["io_aware_softmax_02_amd/build.py"]
 
 
