@@ -51,8 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_b1h16_n8192_d128_hbm_tr
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warm-up steps, so that the "
                          "shader clock has left its idle state (0 to skip)")
