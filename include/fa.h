@@ -121,8 +121,8 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
  * all -inf gets o = 0, lse = -inf.
  * o_part float32 [n_split][B][H][N][d], lse_part float32 [n_split][B][H][N]
  * (inputs); o bf16 [B][H][N][d], lse float32 [B][H][N] (outputs).  d must be
- * 64 or 128; n_split >= 1; 16-byte alignment; outputs may not overlap the
- * inputs (FA_ERR_ALIAS). */
+ * 64 or 128; 1 <= n_split <= 2^24 (else FA_ERR_SHAPE); 16-byte alignment;
+ * outputs may not overlap the inputs (FA_ERR_ALIAS). */
 fa_status fa_merge(const float* o_part, const float* lse_part, int64_t n_split, void* o,
                    float* lse, int64_t B, int64_t H, int64_t N, int64_t d, fa_stream_t stream);
 

@@ -104,10 +104,14 @@ inline int64_t split_max(const Shape& s, int64_t tile) {
   return (s.N + tile - 1) / tile;
 }
 
-// n_split partial tensors of the shape: the count must be >= 1 and the
-// partials must stay inside the size limit.
+// Most partial results a merge takes: the kernels count parts in int32 (in
+// steps of 8), and the split forward makes fewer than 2^24 ranges.
+constexpr int64_t kMaxParts = int64_t(1) << 24;
+
+// n_split partial tensors of the shape: the count must be in [1, kMaxParts]
+// and the partials must stay inside the size limit.
 inline fa_status check_parts(const Shape& s, int64_t n_split) {
-  if (n_split < 1) return FA_ERR_SHAPE;
+  if (n_split < 1 || n_split > kMaxParts) return FA_ERR_SHAPE;
   if (s.empty()) return FA_OK;
   if (n_split > kMaxElems / s.elems()) return FA_ERR_SHAPE;
   return FA_OK;

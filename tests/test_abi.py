@@ -130,6 +130,11 @@ def test_split_and_merge_argument_checks(lib):
     assert split(ptrs=[P[0], P[1], P[2], P[3], P[3] + 2 * 1000 * 128 * 4 - 16]) == L.FA_ERR_ALIAS
     assert split(ptrs=[P[0], P[1], P[2], P[0] + 16, P[4]]) == L.FA_ERR_ALIAS
     assert merge(n=0) == L.FA_ERR_SHAPE
+    # counts beyond 2^24 are refused before anything else (the kernels count
+    # parts in int32); the largest passes on to the pointer checks
+    assert merge(n=(1 << 24) + 1, ptrs=[P[0], 0, P[2], P[3]]) == L.FA_ERR_SHAPE
+    assert merge(n=(1 << 31) + 7, ptrs=[P[0], 0, P[2], P[3]]) == L.FA_ERR_SHAPE
+    assert merge(n=1 << 24, ptrs=[P[0], 0, P[2], P[3]]) == L.FA_ERR_NULL
     assert merge(ptrs=[P[0], 0, P[2], P[3]]) == L.FA_ERR_NULL
     assert merge(ptrs=[P[0], P[1], P[2] + 8, P[3]]) == L.FA_ERR_ALIGN
     assert merge(d=32) == L.FA_ERR_UNSUPPORTED
