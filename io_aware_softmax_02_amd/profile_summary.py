@@ -259,7 +259,7 @@ def cpu_md(path: str) -> str:
     rows = list(_json_lines(path))
     cores = sorted({r["cores"] for r in rows})
     out = ["# The fp64 oracle on the host cores, every named workload\n",
-           "Command (repository root, on the GPU box's host; no GPU work): "
+           "Command (repository root, on the host CPUs of the MI355X machine; no GPU work): "
            "`python bench.py --cpu-configs > LOG; "
            "python -m io_aware_softmax_02_amd.profile_summary cpu LOG`\n",
            "The oracle as it stands (numpy float64, materialising S and P), timed on a bounded "
