@@ -131,7 +131,6 @@ def cpu_configs(args):
     sampled query rows against all keys.  Each line states the sample; the
     per-row time scaled to all rows and heads is labelled as an
     extrapolation."""
-    import numpy as np
     import oracle
     import synth
     f64 = synth.to_f64
@@ -173,7 +172,6 @@ def cpu_configs(args):
                          "extrapolated_all_heads_seconds": round(dt * BH / nh, 1)})
         print(json.dumps(line), flush=True)
         del q, k, v, dO, qf, kf, vf
-    del np
 
 
 def host_cores():
