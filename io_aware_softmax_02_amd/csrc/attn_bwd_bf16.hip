@@ -23,6 +23,8 @@
 // buffer->LDS loads (reads past the end of a head return 0, which is what a
 // ragged last tile needs): dQ double-buffers its K/V tiles with one barrier
 // per tile; dK/dV triple-buffers its Q/dO tiles (below).
+#include <type_traits>
+
 #include "launch_chunks.h"
 #include "lds_tile.h"
 
@@ -517,7 +519,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   wait_vmem();
   __syncthreads();
 
-  for (int it = 0; it < nkt; ++it) {
+  // One key tile; `ragged` (a compile-time flag) is set only for a last tile
+  // that holds keys past N, so that the full tiles carry no masking code.
+  auto tile = [&](int it, auto ragged) {
     uint32_t bo = (uint32_t)((it & 1) * C::BUF_ELEMS * 2);
     asm volatile("" : "+s"(bo));
     const uint8_t* kt8 = reinterpret_cast<const uint8_t*>(smem) + bo;
@@ -572,15 +576,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       // would be 2^(-LSE log2 e), which overflows when every score of the
       // row is below about -88.  They do not exist: their scores are -inf,
       // so P and dS are 0.
-      const int key0 = it * C::BK + kb2 * 32;
-      if (key0 + 32 > N) {
+      if constexpr (decltype(ragged)::value) {
+        const int key0 = it * C::BK + kb2 * 32;
+        if (key0 + 32 > N) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (key0 + 16 * h + 4 * g + i >= N) s[qb][h][i] = -INFINITY;
+              for (int i = 0; i < 4; ++i)
+                if (key0 + 16 * h + 4 * g + i >= N) s[qb][h][i] = -INFINITY;
+        }
       }
       bf16x8 sb[2];
 #pragma unroll
@@ -615,7 +621,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
     wait_vmem();
     __syncthreads();
-  }
+  };
+  const int nfull = N / C::BK;   // tiles whose keys are all < N
+  for (int it = 0; it < nfull; ++it) tile(it, std::false_type{});
+  if (nfull < nkt) tile(nfull, std::true_type{});
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
