@@ -25,14 +25,42 @@ constexpr int T = 8;        // rows per tile (queries and keys)
 constexpr int DMAX = 128;   // largest head dim of the fp32 path
 constexpr int CPT = DMAX / T;  // columns per thread
 
-// Loads rows [r0, r0+T) of a [N][d] matrix into a [T][DMAX] LDS tile; rows at
-// or past N are zero.
+// One thread's share of a T-row tile of a [N][d] matrix: row t / 8, columns
+// t % 8 + 8u (no division by the runtime d; eight threads read 32
+// consecutive bytes).  Rows at or past N are zero.  fetch_tile loads it into
+// registers, put_tile writes it to a [T][DMAX] LDS tile, so that the next
+// tile's loads are in flight while the current tile is used.
+struct TileRegs {
+  float x[CPT];
+};
+
+__device__ __forceinline__ void fetch_tile(TileRegs& tr, const float* src, int r0, int N,
+                                           int d) {
+  static_assert(T * T == 64, "one wave: T rows of T threads");
+  const int r = threadIdx.x >> 3, c0 = threadIdx.x & 7;
+  const bool live = r0 + r < N;
+  const float* row = src + (int64_t)(live ? r0 + r : 0) * d;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = c0 + T * u;
+    tr.x[u] = (live && c < d) ? row[c] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void put_tile(float (*dst)[DMAX], const TileRegs& tr, int d) {
+  const int r = threadIdx.x >> 3, c0 = threadIdx.x & 7;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = c0 + T * u;
+    if (c < d) dst[r][c] = tr.x[u];
+  }
+}
+
 __device__ __forceinline__ void load_tile(float (*dst)[DMAX], const float* src, int r0, int N,
                                           int d) {
-  for (int idx = threadIdx.x; idx < T * d; idx += 64) {
-    const int r = idx / d, c = idx - (idx / d) * d;
-    dst[r][c] = (r0 + r < N) ? src[(int64_t)(r0 + r) * d + c] : 0.0f;
-  }
+  TileRegs tr;
+  fetch_tile(tr, src, r0, N, d);
+  put_tile(dst, tr, d);
 }
 
 __device__ __forceinline__ float group8_max(float x) {
@@ -47,10 +75,42 @@ __device__ __forceinline__ float group8_sum(float x) {
   return x + __shfl_xor(x, 4);
 }
 
+// Dot products of two rows of d floats with four partial sums: element c
+// goes to sum c % 4 (in order of c), and the result is (s0 + s1) + (s2 + s3),
+// so the products do not wait on one accumulator chain.  dot_rows_lds reads
+// 16 bytes at a time from LDS rows (16-byte aligned); dot_rows reads one
+// float at a time (rows in device memory are only 4-byte aligned on this
+// path).  Both sum in the same order: the same two rows give the same float.
 __device__ __forceinline__ float dot_rows(const float* a, const float* b, int d) {
-  float s = 0.0f;
-  for (int c = 0; c < d; ++c) s = fmaf(a[c], b[c], s);
-  return s;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int c = 0;
+  for (; c + 4 <= d; c += 4) {
+    s0 = fmaf(a[c], b[c], s0);
+    s1 = fmaf(a[c + 1], b[c + 1], s1);
+    s2 = fmaf(a[c + 2], b[c + 2], s2);
+    s3 = fmaf(a[c + 3], b[c + 3], s3);
+  }
+  if (c < d) s0 = fmaf(a[c], b[c], s0);
+  if (c + 1 < d) s1 = fmaf(a[c + 1], b[c + 1], s1);
+  if (c + 2 < d) s2 = fmaf(a[c + 2], b[c + 2], s2);
+  return (s0 + s1) + (s2 + s3);
+}
+
+__device__ __forceinline__ float dot_rows_lds(const float* a, const float* b, int d) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int c = 0;
+  for (; c + 4 <= d; c += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + c);
+    const float4 y = *reinterpret_cast<const float4*>(b + c);
+    s0 = fmaf(x.x, y.x, s0);
+    s1 = fmaf(x.y, y.y, s1);
+    s2 = fmaf(x.z, y.z, s2);
+    s3 = fmaf(x.w, y.w, s3);
+  }
+  if (c < d) s0 = fmaf(a[c], b[c], s0);
+  if (c + 1 < d) s1 = fmaf(a[c + 1], b[c + 1], s1);
+  if (c + 2 < d) s2 = fmaf(a[c + 2], b[c + 2], s2);
+  return (s0 + s1) + (s2 + s3);
 }
 
 // grid: (ceil(N/8) * B*H); block: 64.  Lane t: query r = t/8, key j = t%8 for
@@ -61,7 +121,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
                                                      float* __restrict__ o,
                                                      float* __restrict__ lse, int N, int d,
                                                      int ntq, float scale) {
-  __shared__ float Qs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  __shared__ __attribute__((aligned(16))) float Qs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
   const int bh = blockIdx.x / ntq, qt = blockIdx.x - bh * ntq;
   const int64_t base = (int64_t)bh * N * d;
   const int t = threadIdx.x, r = t >> 3, j = t & 7;
@@ -72,12 +132,19 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
 #pragma unroll
   for (int u = 0; u < CPT; ++u) acc[u] = 0.0f;
   const int nkt = (N + T - 1) / T;
+  TileRegs kr, vr;
+  fetch_tile(kr, k + base, 0, N, d);
+  fetch_tile(vr, v + base, 0, N, d);
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
-    load_tile(Ks, k + base, kt * T, N, d);
-    load_tile(Vs, v + base, kt * T, N, d);
+    put_tile(Ks, kr, d);
+    put_tile(Vs, vr, d);
     __syncthreads();
-    float s = scale * dot_rows(Qs[r], Ks[j], d);
+    if (kt + 1 < nkt) {
+      fetch_tile(kr, k + base, (kt + 1) * T, N, d);
+      fetch_tile(vr, v + base, (kt + 1) * T, N, d);
+    }
+    float s = scale * dot_rows_lds(Qs[r], Ks[j], d);
     if (kt * T + j >= N) s = -INFINITY;
     const float m_new = fmaxf(m, group8_max(s));
     const float alpha = expf(m - m_new);  // exp(-inf) = 0 on the first block
@@ -137,7 +204,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     const float* __restrict__ lse, const float* __restrict__ dO,
     const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv, int N,
     int d, int nkt, float scale) {
-  __shared__ float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  __shared__ __attribute__((aligned(16))) float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
   __shared__ float lse_s[T], d_s[T];
   const int bh = blockIdx.x / nkt, kt = blockIdx.x - bh * nkt;
   const int64_t base = (int64_t)bh * N * d;
@@ -151,15 +218,29 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
 #pragma unroll
   for (int u = 0; u < CPT; ++u) accK[u] = accV[u] = 0.0f;
   const int nqt = (N + T - 1) / T;
+  TileRegs qr, gr;
+  float st_l, st_d;   // LSE and D of query row t (threads t < T)
+  auto fetch_q = [&](int q0) {
+    fetch_tile(qr, q + base, q0, N, d);
+    fetch_tile(gr, dO + base, q0, N, d);
+    const bool ok = t < T && q0 + t < N;
+    st_l = ok ? lse_h[q0 + t] : INFINITY;
+    st_d = ok ? delta_h[q0 + t] : 0.0f;
+  };
+  fetch_q(0);
   for (int qt = 0; qt < nqt; ++qt) {
     __syncthreads();
-    load_tile(Qs, q + base, qt * T, N, d);
-    load_tile(dOs, dO + base, qt * T, N, d);
-    load_row_stats(lse_s, d_s, lse_h, delta_h, qt * T, N);
+    put_tile(Qs, qr, d);
+    put_tile(dOs, gr, d);
+    if (t < T) {
+      lse_s[t] = st_l;
+      d_s[t] = st_d;
+    }
     __syncthreads();
-    const float s = scale * dot_rows(Qs[i], Ks[j], d);
+    if (qt + 1 < nqt) fetch_q((qt + 1) * T);
+    const float s = scale * dot_rows_lds(Qs[i], Ks[j], d);
     const float p = expf(s - lse_s[i]);
-    const float dp = dot_rows(dOs[i], Vs[j], d);
+    const float dp = dot_rows_lds(dOs[i], Vs[j], d);
     const float ds = p * (dp - d_s[i]);
     for (int ii = 0; ii < T; ++ii) {
       const float pi = __shfl(p, j * T + ii);
@@ -195,7 +276,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
     const float* __restrict__ lse, const float* __restrict__ dO,
     const float* __restrict__ delta, float* __restrict__ dq, int N, int d, int nqt,
     float scale) {
-  __shared__ float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
+  __shared__ __attribute__((aligned(16))) float Qs[T][DMAX], dOs[T][DMAX], Ks[T][DMAX], Vs[T][DMAX];
   __shared__ float lse_s[T], d_s[T];
   const int bh = blockIdx.x / nqt, qt = blockIdx.x - bh * nqt;
   const int64_t base = (int64_t)bh * N * d;
@@ -208,14 +289,21 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
 #pragma unroll
   for (int u = 0; u < CPT; ++u) acc[u] = 0.0f;
   const int nkt = (N + T - 1) / T;
+  TileRegs kr, vr;
+  fetch_tile(kr, k + base, 0, N, d);
+  fetch_tile(vr, v + base, 0, N, d);
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
-    load_tile(Ks, k + base, kt * T, N, d);
-    load_tile(Vs, v + base, kt * T, N, d);
+    put_tile(Ks, kr, d);
+    put_tile(Vs, vr, d);
     __syncthreads();
-    const float s = scale * dot_rows(Qs[i], Ks[j], d);
+    if (kt + 1 < nkt) {
+      fetch_tile(kr, k + base, (kt + 1) * T, N, d);
+      fetch_tile(vr, v + base, (kt + 1) * T, N, d);
+    }
+    const float s = scale * dot_rows_lds(Qs[i], Ks[j], d);
     const float p = (kt * T + j < N) ? expf(s - lse_s[i]) : 0.0f;
-    const float dp = dot_rows(dOs[i], Vs[j], d);
+    const float dp = dot_rows_lds(dOs[i], Vs[j], d);
     const float ds = p * (dp - d_s[i]);
     for (int jj = 0; jj < T; ++jj) {
       const float dsj = __shfl(ds, i * T + jj);
