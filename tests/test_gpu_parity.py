@@ -104,7 +104,11 @@ def test_f32_forward_shapes(B, H, N, d):
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 64, 64), (1, 2, 37, 16), (2, 1, 8, 4),
                                      (1, 1, 1, 8), (1, 1, 17, 128), (1, 1, 1, 64),
-                                     (1, 2, 1000, 128), (2, 1, 333, 64), (1, 1, 2048, 128)])
+                                     (1, 2, 1000, 128), (2, 1, 333, 64), (1, 1, 2048, 128),
+                                     # head dims that are not multiples of 4 (the row
+                                     # dot products' tails), ragged N, several tiles
+                                     (1, 2, 29, 3), (1, 1, 70, 17), (2, 1, 41, 18),
+                                     (1, 1, 300, 33)])
 def test_f32_backward(B, H, N, d):
     say(f"case f32 bwd B={B} H={H} N={N} d={d}")
     q, k, v, dO = synth.make_qkv(B, H, N, d, torch.float32, seed=200 + N + d, backward=True)
