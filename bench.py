@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--configs", action="store_true",
                     help="forward and fwd+bwd throughput on every named workload instead of "
                          "the headline")
+    ap.add_argument("--api-window", action="store_true",
+                    help="run --steps whole steps (fa_fwd, fa_bwd) with every buffer allocated "
+                         "beforehand, inside a roctx range named fa_steps, for a HIP API trace")
     return ap.parse_args()
 
 
@@ -396,6 +399,42 @@ def splitkv(args):
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and packed vector), published
 
 
+def api_window(args):
+    """The bench workload's step (fa_fwd, then fa_bwd) `args.steps` times,
+    with outputs and workspace allocated and one step run beforehand, inside
+    a roctx range named fa_steps.  Under `rocprofv3 --hip-trace
+    --marker-trace` the HIP calls made inside the range are the library's own
+    (plus the binding's device queries): no allocation, no copy, no memset."""
+    import ctypes
+    import torch
+    import io_aware_softmax_02_amd as fa
+    import synth
+    w = synth.WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, dO = (x.to(dev) for x in synth.make_inputs(w))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_fwd(q, k, v, w.scale, o=o, lse=lse)
+        fa.fa_bwd(q, k, v, o, lse, dO, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    roctx = ctypes.CDLL("librocprofiler-sdk-roctx.so")
+    roctx.roctxRangePushA.argtypes = [ctypes.c_char_p]
+    roctx.roctxRangePushA(b"fa_steps")
+    for _ in range(args.steps):
+        step()
+    roctx.roctxRangePop()
+    torch.cuda.synchronize()
+    print(json.dumps({"api_window": True, "steps": args.steps, "workload": WORKLOAD}), flush=True)
+
+
 def fp32(args):
     """Throughput of the fp32 path (fa_fwd_f32 / fa_bwd_f32) on seeded
     N(0,1) inputs, against the published fp32 peak."""
@@ -548,6 +587,8 @@ def main():
         return cpu_configs(args)
     if args.fp32:
         return fp32(args)
+    if args.api_window:
+        return api_window(args)
 
     import torch
     import io_aware_softmax_02_amd as fa

@@ -297,6 +297,40 @@ def splitkv_md(path: str) -> str:
     return "\n".join(out) + "\n"
 
 
+ALLOC_CALLS = ("hipMalloc", "hipFree", "hipMallocAsync", "hipFreeAsync", "hipMallocManaged",
+               "hipHostMalloc", "hipExtMallocWithFlags", "hipMemset", "hipMemsetAsync",
+               "hipMemcpy", "hipMemcpyAsync")
+
+
+def apicalls(trace_dir: str, title: str, cmd: str) -> str:
+    """HIP API calls made on the thread of the roctx range `fa_steps`
+    between its start and end (rocprofv3 CSV output: *_marker_api_trace.csv
+    and *_hip_api_trace.csv in `trace_dir`)."""
+    mk = [r for r in csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*_marker_api_trace.csv"))[0]))
+          if r["Function"] == "fa_steps"][0]
+    t0, t1, tid = int(mk["Start_Timestamp"]), int(mk["End_Timestamp"]), mk["Thread_Id"]
+    inside = collections.Counter()
+    other_threads = 0
+    for r in csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*_hip_api_trace.csv"))[0])):
+        if t0 <= int(r["Start_Timestamp"]) <= t1:
+            if r["Thread_Id"] == tid:
+                inside[r["Function"]] += 1
+            else:
+                other_threads += 1
+    alloc = {k: v for k, v in inside.items() if k.startswith(ALLOC_CALLS)}
+    out = [f"# {title}\n", "Command (run from the repository root on one MI355X):\n", f"```\n{cmd}\n```\n",
+           f"HIP API calls made between the start and the end of the roctx range `fa_steps` "
+           f"({(t1 - t0) / 1000:.1f} µs), on its thread:\n",
+           "| HIP API function | calls |", "|---|---|"]
+    for k, v in sorted(inside.items(), key=lambda kv: (-kv[1], kv[0])):
+        out.append(f"| `{k}` | {v} |")
+    out.append("")
+    out.append(f"Allocation, free, memset or copy calls inside the range: "
+               f"{sum(alloc.values()) if alloc else 0}" + (f" ({alloc})" if alloc else "") + ".")
+    out.append(f"HIP calls on other threads inside the range: {other_threads}.")
+    return "\n".join(out) + "\n"
+
+
 def main(argv: list[str]) -> int:
     if len(argv) < 2:
         print(__doc__)
@@ -320,6 +354,8 @@ def main(argv: list[str]) -> int:
         sys.stdout.write(sweep_md(argv[2]))
     elif cmd == "splitkv":
         sys.stdout.write(splitkv_md(argv[2]))
+    elif cmd == "apicalls":
+        sys.stdout.write(apicalls(argv[2], argv[3], argv[4]))
     elif cmd == "traffic":
         doc = traffic(argv[2], argv[3], argv[4])
         for k, v in doc["kernels"].items():

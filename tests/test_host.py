@@ -97,3 +97,22 @@ def test_traffic_calibration_uses_only_the_large_copy(tmp_path):
     p = tmp_path / "c.csv"
     p.write_text("\n".join(rows) + "\n")
     assert calibration(str(p), "FETCH_SIZE") == 262158.0
+
+
+def test_apicalls_counts_calls_inside_the_marker_range(tmp_path):
+    """The HIP-call summary counts only calls that start inside the roctx
+    range fa_steps, on the range's thread, and reports allocation calls."""
+    from io_aware_softmax_02_amd import profile_summary as ps
+    hdr = '"Domain","Function","Process_Id","Thread_Id","Correlation_Id","Start_Timestamp","End_Timestamp"\n'
+    (tmp_path / "x_marker_api_trace.csv").write_text(
+        hdr + '"MARKER_CORE_RANGE_API","fa_steps",1,7,9,1000,2000\n')
+    rows = [("hipMalloc", 7, 500), ("hipLaunchKernel", 7, 1100), ("hipLaunchKernel", 7, 1900),
+            ("hipGetLastError", 7, 1200), ("hipLaunchKernel", 8, 1500), ("hipFree", 7, 2500),
+            ("hipMemsetAsync", 7, 1300)]
+    (tmp_path / "x_hip_api_trace.csv").write_text(hdr + "".join(
+        f'"HIP_RUNTIME_API","{f}",1,{t},1,{s},{s + 10}\n' for f, t, s in rows))
+    md = ps.apicalls(str(tmp_path), "T", "C")
+    assert "| `hipLaunchKernel` | 2 |" in md and "| `hipGetLastError` | 1 |" in md
+    assert "hipMalloc" not in md and "hipFree" not in md
+    assert "Allocation, free, memset or copy calls inside the range: 1 ({'hipMemsetAsync': 1})." in md
+    assert "HIP calls on other threads inside the range: 1." in md
