@@ -415,11 +415,12 @@ def test_bf16_forward_is_deterministic():
         assert torch.equal(O, O0) and torch.equal(L, L0)
 
 
-def test_bf16_backward_is_deterministic_and_stages_match():
-    say("case bf16 backward determinism and stage entry points")
-    q, k, v, dO = (gpu(x) for x in synth.make_qkv(1, 3, 1000, 128, torch.bfloat16, 21,
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_backward_is_deterministic_and_stages_match(d):
+    say(f"case bf16 backward determinism and stage entry points d={d}")
+    q, k, v, dO = (gpu(x) for x in synth.make_qkv(1, 3, 1000, d, torch.bfloat16, 21,
                                                    backward=True))
-    s = synth.default_scale(128)
+    s = synth.default_scale(d)
     O, L = fa.fa_fwd(q, k, v, s)
     ref = fa.fa_bwd(q, k, v, O, L, dO, s)
     for _ in range(5):
